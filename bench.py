@@ -1,0 +1,195 @@
+"""Benchmark: one MI355X's share of exact causal ring attention.
+
+A step is one pass of the hot path over one batch of synthetic input: the
+zig-zag placement of Q, K and V into shards (zigzag_partition), then every
+shard's queries against its c key/value blocks in ring order
+(ring_attn_shard_fwd), the shards run one after another on one GPU.
+Inputs are resident in HBM before the timed region starts.
+
+Prints one JSON line: causal-useful TFLOP/s (4 * d * visible pairs per query
+head, summed over shards, divided by step time), the roofline entry of the
+attention kernel (MFMA bf16 dense peak), and the fp64 oracle timed on a
+bounded sample on the host's cores as a CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+METRIC = "causal attention TFLOP/s per shard on 1 MI355X + % of bf16 MFMA peak"
+# MI355X bf16 dense matrix peak: 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU.
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
+PEAK_F32_TFLOPS = 157.3
+
+
+def useful_flop(w, pairs_per_head):
+    return 4.0 * w.head_dim * w.h_q * w.batch * pairs_per_head
+
+
+def cpu_baseline(w, target_s):
+    """The fp64 oracle on a bounded row sample of shard 0 (one query head)."""
+    import oracle
+    q_pos_all = oracle.partition_perm(w.seq_len, w.n_shards, w.split)[:w.n_loc]
+    # Rows spread over the whole shard so the sample's mix of early and late
+    # tokens matches the shard's.
+    g = np.random.default_rng(0)
+    order = g.permutation(w.n_loc)
+    q, k, v = workloads.draw_qkv(w, positions=None) if w.seq_len <= 8192 else (None, None, None)
+    if q is None:
+        k = workloads.draw(w.seed, workloads.TENSOR_K, w.batch, w.h_kv, w.seq_len, w.head_dim, w.sigma, w.dtype)
+        v = workloads.draw(w.seed, workloads.TENSOR_V, w.batch, w.h_kv, w.seq_len, w.head_dim, w.sigma, w.dtype)
+    done_rows, flop, elapsed, n = 0, 0.0, 0.0, 16
+    while elapsed < target_s and done_rows < w.n_loc:
+        rows_local = order[done_rows:done_rows + n]
+        pos = q_pos_all[rows_local]
+        qs = workloads.draw(w.seed, workloads.TENSOR_Q, w.batch, 1, w.seq_len, w.head_dim, w.sigma, w.dtype,
+                            positions=pos) if w.seq_len > 8192 else q[:, :1, pos]
+        t0 = time.perf_counter()
+        oracle.attention(qs, k[:, :1], v[:, :1], w.scale, w.causal, q_pos=pos)
+        elapsed += time.perf_counter() - t0
+        flop += 4.0 * w.head_dim * w.batch * float((pos + 1).sum() if w.causal else len(pos) * w.seq_len)
+        done_rows += len(rows_local)
+        if elapsed < target_s / 4:
+            n *= 2
+    return {"value": flop / elapsed / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{done_rows} query rows of shard 0, query head 0, all their visible keys "
+                      f"({flop / 1e9:.1f} GFLOP useful in {elapsed:.1f} s, fp64)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="s128k_c16_zigzag_16x1", choices=sorted(workloads.WORKLOAD_BY_NAME))
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle CPU-baseline budget (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the ring: run with --gpus 1 (got {args.gpus}); "
+              "the multi-GPU ring is not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import ring_parallelism_amd as ra
+
+    w = workloads.WORKLOAD_BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    in_dt = ra.BF16 if w.dtype == "bf16" else ra.F32
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        return (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if w.dtype == "bf16"
+                else torch.from_numpy(a)).to(dev)
+
+    q, k, v = workloads.draw_qkv(w)
+    qn, kn, vn = up(q), up(k), up(v)
+    del q, k, v
+    c, n_loc = w.n_shards, w.n_loc
+    qs = torch.empty((c, w.batch, w.h_q, n_loc, w.head_dim), dtype=tdt, device=dev)
+    ks = torch.empty((c, w.batch, w.h_kv, n_loc, w.head_dim), dtype=tdt, device=dev)
+    vs = torch.empty_like(ks)
+    out = torch.empty((w.batch, w.h_q, n_loc, w.head_dim), dtype=tdt, device=dev)
+    lse = torch.empty((w.batch, w.h_q, n_loc), dtype=torch.float32, device=dev)
+    stats = torch.zeros(4, dtype=torch.int64, device=dev)
+    desc = ra.make_desc(w.seq_len, c, w.split, w.batch, w.h_q, w.h_kv, w.head_dim, in_dt, in_dt, w.causal, w.scale)
+    esz = qn.element_size()
+    owners = [[(r - t) % c for t in range(c)] for r in range(c)]
+    kb = [[ks[j] for j in owners[r]] for r in range(c)]
+    vb = [[vs[j] for j in owners[r]] for r in range(c)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(c)]
+
+    def step(timed_kernels):
+        ra.zigzag_partition(w.seq_len, c, w.split, None, qn, qs, w.batch * w.h_q, w.head_dim * esz)
+        ra.zigzag_partition(w.seq_len, c, w.split, None, kn, ks, w.batch * w.h_kv, w.head_dim * esz)
+        ra.zigzag_partition(w.seq_len, c, w.split, None, vn, vs, w.batch * w.h_kv, w.head_dim * esz)
+        for r in range(c):
+            if timed_kernels:
+                ev[r][0].record()
+            ra.ring_attn_shard_fwd(desc, r, qs[r], kb[r], vb[r], out, lse, stats=stats)
+            if timed_kernels:
+                ev[r][1].record()
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    stats.zero_()
+
+    # Timed region: exactly K steps back to back.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(False)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    st = stats.cpu().tolist()
+
+    # Kernel durations with HIP events on the launch stream (a separate pass).
+    kernel_ms = []
+    for _ in range(max(1, min(args.steps, 3))):
+        step(True)
+        torch.cuda.synchronize()
+        kernel_ms.extend(ev[r][0].elapsed_time(ev[r][1]) for r in range(c))
+
+    pairs = [shard_pairs(w, r) for r in range(c)]               # per query head
+    flop_step = sum(useful_flop(w, pr) for pr in pairs)
+    pairs_counted = st[0] / args.steps
+    if abs(pairs_counted - sum(pairs) * w.h_q * w.batch) > 0.5:
+        raise SystemExit(f"kernel pair count {pairs_counted} != {sum(pairs) * w.h_q * w.batch}")
+    ms_step = elapsed * 1e3 / args.steps
+    value = flop_step / (elapsed / args.steps) / 1e12
+    avg_kernel_s = float(np.mean(kernel_ms)) / 1e3
+    flop_launch = flop_step / c
+    achieved = flop_launch / avg_kernel_s / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    res = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "seq_len": w.seq_len, "n_shards": c,
+                   "split": {0: "contiguous", 1: "zigzag", 2: "striped"}[w.split], "batch": w.batch,
+                   "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.head_dim, "causal": w.causal,
+                   "shards_per_step": c, "inputs": f"N(0,{w.sigma}^2) seeded, bf16-rounded" if w.dtype == "bf16" else "N(0,1) seeded"},
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": round(peak, 1),
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "fwd_bf16_kernel" if w.dtype == "bf16" else "fwd_f32_kernel",
+                     "flop_per_launch": flop_launch, "avg_launch_ms": round(avg_kernel_s * 1e3, 4),
+                     "launches_timed": len(kernel_ms)},
+        "stats_per_step": {"pairs": int(pairs_counted), "tiles_full": st[1] // args.steps,
+                           "tiles_partial": st[2] // args.steps, "tiles_skipped": st[3] // args.steps},
+    }
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def shard_pairs(w, r):
+    """Visible (query, key) pairs of shard r for one query head: each token at
+    global position p sees p + 1 keys under the causal mask, S without it."""
+    n_loc = w.n_loc
+    t = np.arange(n_loc, dtype=np.int64)
+    if w.split == workloads.SPLIT_ZIGZAG:
+        n = n_loc // 2
+        pos = np.where(t < n, r * n + t, (2 * w.n_shards - 1 - r) * n + (t - n))
+    elif w.split == workloads.SPLIT_STRIPED:
+        pos = t * w.n_shards + r
+    else:
+        pos = r * n_loc + t
+    return int((pos + 1).sum()) if w.causal else n_loc * w.seq_len
+
+
+if __name__ == "__main__":
+    main()

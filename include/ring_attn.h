@@ -1,0 +1,171 @@
+/* ring_attn.h -- C ABI of the MI355X (gfx950) ring-attention shard library.
+ *
+ * One device's share of exact causal blockwise ring attention.  Each device
+ * holds the queries of its own tokens and sees the key/value blocks of every
+ * device in ring order; each block's partial result is folded in with an
+ * online softmax (running max m, normaliser l, output rescaled when the max
+ * rises) and the output is divided by l at the end ("Sequence / context
+ * parallelism" notes, section 4 "Ring Attention -- the core algorithm";
+ * "Splitting the Sequence", intro).  On one GPU the blocks that would arrive
+ * from the ring neighbours are read from HBM in ring order.
+ *
+ * Conventions shared by every entry point
+ *   - Every function returns ra_status; RA_OK (0) on success.  On failure
+ *     nothing was launched and ring_attn_last_error() describes the cause.
+ *   - Device buffers are owned by the caller; the library allocates no
+ *     device memory, keeps no state between calls and is thread-safe.  Host
+ *     arrays passed in (block_owner, k_blocks, v_blocks, outs, lses) are read
+ *     during the call only.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     on it and the call returns at once; faults surface at the caller's next
+ *     synchronisation.
+ *   - Tensors are dense and row-major with the last dimension contiguous;
+ *     device pointers must be 16-byte aligned (lse and stats: 4 / 8 bytes).
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef RING_ATTN_H
+#define RING_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t ra_status;
+enum {
+  RA_OK = 0,
+  RA_EINVAL = 1,        /* invalid argument (null, divisibility, range, alignment) */
+  RA_EUNSUPPORTED = 2,  /* valid but not implemented (head_dim, dtype pairing, too many blocks) */
+  RA_EHIP = 3           /* the HIP runtime refused a launch */
+};
+
+/* Token placement of the shards.
+ *   CONTIGUOUS: shard r holds tokens [r*S/c, (r+1)*S/c) ("Sequence / context
+ *               parallelism" notes, section 1 diagram).
+ *   ZIGZAG:     the sequence is cut into 2c chunks of n = S/(2c) tokens and
+ *               shard r holds chunks r and 2c-1-r, in that order
+ *               ("Splitting the Sequence", intro and Terms: zig-zag split).
+ *   STRIPED:    round-robin; shard r holds tokens r, r+c, r+2c, ... (notes,
+ *               section 5 "Striped / zigzag attention": interleaved pattern).
+ * Within a shard the tokens keep ascending global position. */
+enum { RA_SPLIT_CONTIGUOUS = 0, RA_SPLIT_ZIGZAG = 1, RA_SPLIT_STRIPED = 2 };
+
+enum { RA_F32 = 0, RA_BF16 = 1 };
+
+#define RA_MAX_BLOCKS 128  /* ring blocks per ring_attn_shard_fwd call */
+#define RA_MAX_PARTS 64    /* partial results per ring_attn_merge call */
+#define RA_ABI_VERSION 1
+
+typedef struct {
+  int64_t seq_len;   /* S, global tokens; S % c == 0 (S % 2c == 0 for ZIGZAG) */
+  int32_t n_shards;  /* c >= 1 */
+  int32_t split;     /* RA_SPLIT_*: fixes the global position of every shard-local token */
+  int32_t batch;     /* B >= 1 */
+  int32_t h_q;       /* query heads */
+  int32_t h_kv;      /* key/value heads; h_q % h_kv == 0 and query head h reads
+                        key/value head h / (h_q / h_kv) (grouped-query attention,
+                        "Splitting the Sequence", intro: 8 KV against 128 query heads) */
+  int32_t head_dim;  /* d: 64 or 128 */
+  int32_t in_dtype;  /* RA_F32 or RA_BF16, the dtype of Q, K and V */
+  int32_t out_dtype; /* RA_F32 or RA_BF16; bf16 inputs may write fp32 out */
+  int32_t causal;    /* 1: key position <= query position (global positions); 0: all keys */
+  float scale;       /* softmax scale applied to q.k: finite and > 0 (e.g. 1/sqrt(d)) */
+} ra_attn_desc;
+
+/* Shard placement and optional gather into shard-major order.
+ *
+ * perm (device int64[S], may be NULL): perm[r*(S/c) + t] = global position
+ *   of shard r's t-th token under `split`.
+ * src, dst (device, both NULL or both set): src viewed as
+ *   [outer][S][inner_bytes] in natural token order, dst as
+ *   [c][outer][S/c][inner_bytes]; dst[r][o][t] = src[o][perm[r*(S/c)+t]].
+ *   With a [B, H, S, d] tensor: outer = B*H, inner_bytes = d * element size,
+ *   and dst[r] is shard r's [B, H, S/c, d] tensor.  src and dst must not
+ *   overlap.
+ * Errors: RA_EINVAL for S < 1, c < 1, S not divisible as `split` needs,
+ *   unknown split, perm == src == NULL, outer < 1 or inner_bytes < 1 with a
+ *   gather, or misaligned pointers. */
+ra_status zigzag_partition(int64_t seq_len, int32_t n_shards, int32_t split, int64_t* perm,
+                           const void* src, void* dst, int64_t outer, int64_t inner_bytes,
+                           void* stream);
+
+/* The inverse placement: scatter shard-major rows back to natural order.
+ * src viewed as [c][outer][S/c][inner_bytes], dst as [outer][S][inner_bytes];
+ * dst[o][perm[r*(S/c)+t]] = src[r][o][t].  Same errors as zigzag_partition. */
+ra_status zigzag_unpartition(int64_t seq_len, int32_t n_shards, int32_t split,
+                             const void* src, void* dst, int64_t outer, int64_t inner_bytes,
+                             void* stream);
+
+/* One shard's queries against a sequence of key/value blocks.
+ *
+ * rank         : the shard r in [0, c) whose queries q holds.
+ * q            : device [B, h_q, S/c, d] in_dtype, shard r's tokens in shard order.
+ * n_blocks     : number of blocks to fold, 1..min(c, RA_MAX_BLOCKS).
+ * block_owner  : host int32[n_blocks], the shard each block belongs to, in
+ *                visiting order; distinct values in [0, c).  NULL = ring
+ *                order owner[t] = (r - t) mod c, t = 0..n_blocks-1 (at step t
+ *                a device holds the block that started t hops upstream).
+ * k_blocks,
+ * v_blocks     : host arrays of n_blocks device pointers; block t is shard
+ *                block_owner[t]'s keys / values, [B, h_kv, S/c, d] in_dtype.
+ * out          : device [B, h_q, S/c, d] out_dtype.  With all c blocks it is
+ *                the exact attention output of the shard's queries; with a
+ *                subset, the partial result over those keys only.
+ * lse          : device fp32 [B, h_q, S/c]: natural log of the sum of
+ *                exp(scale * q.k) over the visible keys of the folded
+ *                blocks; -inf (with out = 0) for a row that sees none.
+ * stats        : device int64[4] or NULL; atomically ADDED to:
+ *                [0] visible (query, key) pairs summed over batch and query
+ *                    heads, [1] full tiles, [2] partially masked tiles,
+ *                [3] skipped (fully masked) tiles; tiles are
+ *                ring_attn_tile_shape() query rows x key rows of one block,
+ *                counted per (batch, query head).
+ * Errors: RA_EINVAL for a bad descriptor (see ra_attn_desc), rank or
+ *   n_blocks out of range, owners out of range or repeated, null or
+ *   misaligned pointers; RA_EUNSUPPORTED for head_dim not 64/128, f32 inputs
+ *   with bf16 output, S >= 2^31 - 1 or S/c * d >= 2^31; RA_EHIP on launch
+ *   failure. */
+ra_status ring_attn_shard_fwd(const ra_attn_desc* desc, int32_t rank, const void* q,
+                              int32_t n_blocks, const int32_t* block_owner,
+                              const void* const* k_blocks, const void* const* v_blocks,
+                              void* out, float* lse, int64_t* stats, void* stream);
+
+/* Tile shape (query rows, keys) that ring_attn_shard_fwd uses for `desc`,
+ * i.e. the unit its stats count.  Errors as for the descriptor checks. */
+ra_status ring_attn_tile_shape(const ra_attn_desc* desc, int32_t* tile_q, int32_t* tile_k);
+
+/* n-way merge of partial results over disjoint key sets.
+ *
+ * For each of batch*heads*rows rows: LSE = log sum_k exp(lse_k) and
+ * out = sum_k exp(lse_k - LSE) * out_k; parts with lse_k = -inf carry no
+ * keys, and a row whose parts are all -inf gives (0, -inf).  This is the fold
+ * each ring step applies ("Sequence / context parallelism" notes, section 4).
+ *
+ * outs  : host array of n_parts device pointers, each [batch, heads, rows,
+ *         head_dim] of parts_dtype.
+ * lses  : host array of n_parts device pointers, each fp32 [batch, heads, rows].
+ * out   : device [batch, heads, rows, head_dim] out_dtype; lse: device fp32
+ *         [batch, heads, rows].  out may be outs[0] and lse may be lses[0]
+ *         (in-place accumulation); no other overlap is allowed.
+ * Errors: RA_EINVAL for n_parts not in 1..RA_MAX_PARTS, any size < 1, null or
+ *   misaligned pointers, unknown dtypes; RA_EUNSUPPORTED for head_dim that is
+ *   not a multiple of 4 dividing 256 (each row is then handled inside one
+ *   wavefront, which is what makes the in-place aliasing safe); RA_EHIP on
+ *   launch failure. */
+ra_status ring_attn_merge(int32_t batch, int32_t heads, int64_t rows, int32_t head_dim,
+                          int32_t n_parts, const void* const* outs, int32_t parts_dtype,
+                          const float* const* lses, void* out, int32_t out_dtype, float* lse,
+                          void* stream);
+
+/* Message for the last non-OK status returned on this thread. */
+const char* ring_attn_last_error(void);
+
+/* RA_ABI_VERSION of the loaded library. */
+int32_t ring_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RING_ATTN_H */

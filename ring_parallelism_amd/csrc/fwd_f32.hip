@@ -1,0 +1,156 @@
+// fp32 shard forward: plain VALU kernel, one query row per lane.
+//
+// The online-softmax fold over ring-ordered key/value blocks ("Sequence /
+// context parallelism" notes, section 4): per key tile, raise the running
+// max m, rescale the running normaliser l and output accumulator by
+// exp(m_old - m_new), add the tile's exp(s - m_new) terms, and divide by l at
+// the end.  Everything stays in fp32 (no reduced-precision products), which
+// is what a 1e-5 absolute bound against fp64 needs.
+//
+// Workgroup = one wavefront = TQ query rows of one (batch, head).  Key/value
+// tiles of TK rows are staged in LDS and read as broadcasts.  Tiles whose
+// keys all follow the workgroup's last query are skipped without being read.
+#include "ra_common.h"
+
+namespace ra {
+namespace {
+
+constexpr int TQ = 64;
+constexpr int TK = 32;
+
+template <int D>
+__global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
+  __shared__ float ks[TK][D];
+  __shared__ float vs[TK][D];
+
+  const int lane = threadIdx.x;
+  const int w = blockIdx.x;
+  const int qt = w % p.n_qtiles;
+  const int h = (w / p.n_qtiles) % p.h_q;
+  const int b = w / (p.n_qtiles * p.h_q);
+  const int hk = h / p.group;
+  const int64_t n_loc = p.n_loc;
+
+  const int64_t i0 = (int64_t)qt * TQ;
+  const int64_t row = i0 + lane;
+  const bool row_ok = row < n_loc;
+  const int64_t last_row = (i0 + TQ <= n_loc ? i0 + TQ : n_loc) - 1;
+  const bool rows_full = i0 + TQ <= n_loc;
+  const int64_t pos_q = row_ok ? token_pos(p.rank, row, n_loc, p.c, p.split) : -1;
+  const int64_t pos_first = token_pos(p.rank, i0, n_loc, p.c, p.split);
+  const int64_t pos_last = token_pos(p.rank, last_row, n_loc, p.c, p.split);
+
+  const float* qp = (const float*)p.q + (((int64_t)b * p.h_q + h) * n_loc + (row_ok ? row : 0)) * D;
+  float qv[D], o[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    qv[e] = row_ok ? qp[e] : 0.f;
+    o[e] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  unsigned long long pairs = 0, t_full = 0, t_part = 0, t_skip = 0;
+
+  for (int t = 0; t < p.n_blocks; ++t) {
+    const int j = p.owner[t];
+    const int64_t kv_off = ((int64_t)b * p.h_kv + hk) * n_loc * D;
+    const float* kp = (const float*)p.k[t] + kv_off;
+    const float* vp = (const float*)p.v[t] + kv_off;
+    const int64_t c_last = p.causal ? count_upto(j, pos_last, n_loc, p.c, p.split) : n_loc;
+    const int64_t c_first = p.causal ? count_upto(j, pos_first, n_loc, p.c, p.split) : n_loc;
+    const int n_vis = (int)((c_last + TK - 1) / TK);
+    const int n_full = rows_full ? (int)(c_first / TK) : 0;
+    t_full += n_full;
+    t_part += n_vis - n_full;
+    t_skip += p.n_ktiles - n_vis;
+
+    for (int kt = 0; kt < n_vis; ++kt) {
+      const int64_t key0 = (int64_t)kt * TK;
+      __syncthreads();
+      for (int idx = lane; idx < TK * D; idx += 64) {
+        const int kk = idx / D, e = idx % D;
+        const bool ok = key0 + kk < n_loc;
+        ks[kk][e] = ok ? kp[(key0 + kk) * D + e] : 0.f;
+        vs[kk][e] = ok ? vp[(key0 + kk) * D + e] : 0.f;
+      }
+      __syncthreads();
+
+      const bool masked = kt >= n_full;
+      float s[TK];
+      float mt = -INFINITY;
+#pragma unroll 4
+      for (int kk = 0; kk < TK; ++kk) {
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < D; ++e) dot = fmaf(qv[e], ks[kk][e], dot);
+        bool vis = true;
+        if (masked) {
+          const int64_t jj = key0 + kk;
+          vis = row_ok && jj < n_loc &&
+                (!p.causal || token_pos(j, jj, n_loc, p.c, p.split) <= pos_q);
+          pairs += vis ? 1 : 0;
+        }
+        s[kk] = vis ? dot * p.scale : -INFINITY;
+        mt = fmaxf(mt, s[kk]);
+      }
+      if (!masked) pairs += TK;
+      const float m_new = fmaxf(m, mt);
+      if (m_new == -INFINITY) continue;  // nothing visible to this row yet
+      const float alpha = expf(m - m_new);  // m = -inf gives 0
+      l *= alpha;
+#pragma unroll
+      for (int e = 0; e < D; ++e) o[e] *= alpha;
+#pragma unroll 4
+      for (int kk = 0; kk < TK; ++kk) {
+        const float pk = expf(s[kk] - m_new);
+        l += pk;
+#pragma unroll
+        for (int e = 0; e < D; ++e) o[e] = fmaf(pk, vs[kk][e], o[e]);
+      }
+      m = m_new;
+    }
+  }
+
+  if (row_ok) {
+    const int64_t ro = ((int64_t)b * p.h_q + h) * n_loc + row;
+    float* op = (float*)p.out + ro * D;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int e = 0; e < D; ++e) op[e] = o[e] * inv;
+    p.lse[ro] = l > 0.f ? m + logf(l) : -INFINITY;
+  }
+
+  if (p.stats) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) pairs += __shfl_xor(pairs, off);
+    if (lane == 0) {
+      atomicAdd(p.stats + 0, pairs);
+      atomicAdd(p.stats + 1, t_full);
+      atomicAdd(p.stats + 2, t_part);
+      atomicAdd(p.stats + 3, t_skip);
+    }
+  }
+}
+
+}  // namespace
+
+void tile_shape_f32(int32_t head_dim, int32_t* tq, int32_t* tk) {
+  (void)head_dim;
+  *tq = TQ;
+  *tk = TK;
+}
+
+hipError_t launch_fwd_f32(const FwdParams& p0, int32_t head_dim, hipStream_t stream) {
+  FwdParams p = p0;
+  p.n_qtiles = (int32_t)((p.n_loc + TQ - 1) / TQ);
+  p.n_ktiles = (int32_t)((p.n_loc + TK - 1) / TK);
+  p.n_pairs = p.n_qtiles;
+  const int64_t grid = (int64_t)p.batch * p.h_q * p.n_qtiles;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (head_dim == 64)
+    hipLaunchKernelGGL(fwd_f32_kernel<64>, dim3((unsigned)grid), dim3(64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(fwd_f32_kernel<128>, dim3((unsigned)grid), dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace ra

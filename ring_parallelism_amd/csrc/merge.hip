@@ -1,0 +1,97 @@
+// Merge of partial (out, lse) results over disjoint key sets.
+//
+// LSE = log sum_k exp(lse_k), out = sum_k exp(lse_k - LSE) out_k: the fold a
+// ring step applies to the state it carries ("Sequence / context
+// parallelism" notes, section 4).  Parts with lse = -inf hold no keys; a row
+// whose parts are all -inf yields (0, -inf).
+//
+// HBM-bound: each thread owns 4 consecutive elements of one row (16-byte fp32
+// or 8-byte bf16 accesses), consecutive threads walk a row and then the next
+// row, so every wavefront reads and writes contiguous memory.  The per-row
+// weights are recomputed by each of the row's threads from the n lse values
+// (a few scalars, cached).
+#include "ra_common.h"
+
+namespace ra {
+namespace {
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+__device__ inline float4 load4(const void* base, int64_t idx) {
+  if constexpr (sizeof(T) == 4) {
+    return *(const float4*)((const float*)base + idx);
+  } else {
+    const bf16x4 v = *(const bf16x4*)((const __bf16*)base + idx);
+    return float4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+  }
+}
+
+template <typename T>
+__device__ inline void store4(void* base, int64_t idx, float4 x) {
+  if constexpr (sizeof(T) == 4) {
+    *(float4*)((float*)base + idx) = x;
+  } else {
+    bf16x4 v;
+    v[0] = (__bf16)x.x;
+    v[1] = (__bf16)x.y;
+    v[2] = (__bf16)x.z;
+    v[3] = (__bf16)x.w;
+    *(bf16x4*)((__bf16*)base + idx) = v;
+  }
+}
+
+template <typename PartT, typename OutT>
+__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
+  const int per_row = p.head_dim / 4;
+  const int64_t total = p.n_rows * per_row;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total; u += stride) {
+    const int64_t r = u / per_row;
+    const int64_t idx = r * p.head_dim + (u % per_row) * 4;
+    float mx = -INFINITY;
+    for (int k = 0; k < p.n_parts; ++k) mx = fmaxf(mx, p.lses[k][r]);
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    float z = 0.f;
+    if (mx != -INFINITY) {
+      for (int k = 0; k < p.n_parts; ++k) {
+        const float w = expf(p.lses[k][r] - mx);  // exp(-inf) = 0
+        z += w;
+        if (w != 0.f) {
+          const float4 o = load4<PartT>(p.outs[k], idx);
+          acc.x = fmaf(w, o.x, acc.x);
+          acc.y = fmaf(w, o.y, acc.y);
+          acc.z = fmaf(w, o.z, acc.z);
+          acc.w = fmaf(w, o.w, acc.w);
+        }
+      }
+    }
+    const float inv = z > 0.f ? 1.f / z : 0.f;
+    // Every thread of the row has read its inputs before any write: a thread
+    // only ever writes the elements it read, so out/lse may alias part 0.
+    store4<OutT>(p.out, idx, float4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv});
+    if (u % per_row == 0) p.lse[r] = z > 0.f ? mx + logf(z) : -INFINITY;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_merge(const MergeParams& p, int32_t parts_dtype, int32_t out_dtype,
+                        hipStream_t stream) {
+  const int64_t total = p.n_rows * (p.head_dim / 4);
+  int64_t grid = (total + 255) / 256;
+  if (grid > 256 * 64) grid = 256 * 64;
+  if (grid < 1) grid = 1;
+  const dim3 gd((unsigned)grid), bd(256);
+  if (parts_dtype == RA_F32 && out_dtype == RA_F32)
+    hipLaunchKernelGGL((merge_kernel<float, float>), gd, bd, 0, stream, p);
+  else if (parts_dtype == RA_F32)
+    hipLaunchKernelGGL((merge_kernel<float, __bf16>), gd, bd, 0, stream, p);
+  else if (out_dtype == RA_F32)
+    hipLaunchKernelGGL((merge_kernel<__bf16, float>), gd, bd, 0, stream, p);
+  else
+    hipLaunchKernelGGL((merge_kernel<__bf16, __bf16>), gd, bd, 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace ra

@@ -1,0 +1,108 @@
+// Internal definitions shared by the library's kernels and host code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ring_attn.h"
+
+namespace ra {
+
+// Global position of local token t of shard r (n_loc = S/c tokens per
+// shard).  Positions ascend with t for every split, which the kernels use to
+// classify a tile from its first and last row alone.
+//   contiguous: r*n_loc + t
+//   zig-zag:    chunk r then chunk 2c-1-r of n = n_loc/2 tokens each
+//   striped:    t*c + r
+__host__ __device__ inline int64_t token_pos(int64_t r, int64_t t, int64_t n_loc, int32_t c,
+                                             int32_t split) {
+  if (split == RA_SPLIT_ZIGZAG) {
+    const int64_t n = n_loc >> 1;
+    return t < n ? r * n + t : (2 * (int64_t)c - 1 - r) * n + (t - n);
+  }
+  if (split == RA_SPLIT_STRIPED) return t * c + r;
+  return r * n_loc + t;
+}
+
+__host__ __device__ inline int64_t clamp64(int64_t x, int64_t lo, int64_t hi) {
+  return x < lo ? lo : (x > hi ? hi : x);
+}
+
+// Number of local keys of block j whose global position is <= p.  Because
+// positions ascend within a block, these keys are the block's first
+// count_upto() rows.
+__host__ __device__ inline int64_t count_upto(int64_t j, int64_t p, int64_t n_loc, int32_t c,
+                                              int32_t split) {
+  if (p < 0) return 0;
+  if (split == RA_SPLIT_ZIGZAG) {
+    const int64_t n = n_loc >> 1;
+    return clamp64(p - j * n + 1, 0, n) + clamp64(p - (2 * (int64_t)c - 1 - j) * n + 1, 0, n);
+  }
+  if (split == RA_SPLIT_STRIPED) return p < j ? 0 : clamp64((p - j) / c + 1, 0, n_loc);
+  return clamp64(p - j * n_loc + 1, 0, n_loc);
+}
+
+// 32-bit forms for the attention kernels (global positions < 2^31 there).
+__device__ inline int token_pos32(int r, int t, int n_loc, int c, int split) {
+  if (split == RA_SPLIT_ZIGZAG) {
+    const int n = n_loc >> 1;
+    return t < n ? r * n + t : (2 * c - 1 - r) * n + (t - n);
+  }
+  if (split == RA_SPLIT_STRIPED) return t * c + r;
+  return r * n_loc + t;
+}
+
+__device__ inline int clamp32(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+__device__ inline int count_upto32(int j, int p, int n_loc, int c, int split) {
+  if (p < 0) return 0;
+  if (split == RA_SPLIT_ZIGZAG) {
+    const int n = n_loc >> 1;
+    return clamp32(p - j * n + 1, 0, n) + clamp32(p - (2 * c - 1 - j) * n + 1, 0, n);
+  }
+  if (split == RA_SPLIT_STRIPED) return p < j ? 0 : clamp32((p - j) / c + 1, 0, n_loc);
+  return clamp32(p - j * n_loc + 1, 0, n_loc);
+}
+
+struct FwdParams {
+  const void* q;
+  void* out;
+  float* lse;
+  unsigned long long* stats;
+  int64_t n_loc;       // S / c
+  int32_t c, split, rank, n_blocks;
+  int32_t batch, h_q, h_kv, group;  // group = h_q / h_kv
+  int32_t causal;
+  int32_t n_qtiles;    // ceil(n_loc / tile_q)
+  int32_t n_pairs;     // ceil(n_qtiles / 2): each workgroup takes q-tiles p and n_qtiles-1-p
+  int32_t n_ktiles;    // ceil(n_loc / tile_k)
+  float scale;         // softmax scale
+  float scale_log2;    // scale * log2(e)
+  int32_t owner[RA_MAX_BLOCKS];
+  const void* k[RA_MAX_BLOCKS];
+  const void* v[RA_MAX_BLOCKS];
+};
+
+struct MergeParams {
+  const void* outs[RA_MAX_PARTS];
+  const float* lses[RA_MAX_PARTS];
+  void* out;
+  float* lse;
+  int64_t n_rows;     // batch * heads * rows
+  int32_t head_dim;
+  int32_t n_parts;
+};
+
+// Launchers (defined in the kernel translation units).
+hipError_t launch_partition(int64_t S, int32_t c, int32_t split, int64_t* perm, const void* src,
+                            void* dst, int64_t outer, int64_t inner_bytes, bool inverse,
+                            hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdParams& p, int32_t head_dim, hipStream_t stream);
+hipError_t launch_fwd_bf16(const FwdParams& p, int32_t head_dim, int32_t out_dtype,
+                           hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, int32_t parts_dtype, int32_t out_dtype,
+                        hipStream_t stream);
+void tile_shape_f32(int32_t head_dim, int32_t* tq, int32_t* tk);
+void tile_shape_bf16(int32_t head_dim, int32_t* tq, int32_t* tk);
+
+}  // namespace ra

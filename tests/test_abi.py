@@ -1,0 +1,158 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments before any launch (no GPU needed: every call here fails validation
+or touches no device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import ring_parallelism_amd as ra
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ring_attn.h")
+FAKE = 0x10000  # 64 KiB-aligned fake device address; never dereferenced by a failing call
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:ra_status|const char\*|int32_t)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(ra.EXPORTS)
+    lib = ra.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert ra.abi_version() == 1
+
+
+def good_desc(**kw):
+    d = dict(seq_len=1024, n_shards=4, split=ra.SPLIT_ZIGZAG, batch=1, h_q=4, h_kv=1, head_dim=128,
+             in_dtype=ra.BF16, out_dtype=ra.F32, causal=True, scale=128 ** -0.5)
+    d.update(kw)
+    return ra.AttnDesc(d["seq_len"], d["n_shards"], d["split"], d["batch"], d["h_q"], d["h_kv"],
+                       d["head_dim"], d["in_dtype"], d["out_dtype"], int(d["causal"]), d["scale"])
+
+
+def expect(status, fn, *a, match=None, **kw):
+    with pytest.raises(ra.RingAttnError) as ei:
+        fn(*a, **kw)
+    assert ei.value.status == status, str(ei.value)
+    if match:
+        assert re.search(match, str(ei.value)), str(ei.value)
+
+
+def test_tile_shape():
+    assert ra.ring_attn_tile_shape(good_desc()) == (128, 64)
+    assert ra.ring_attn_tile_shape(good_desc(in_dtype=ra.F32, head_dim=64)) == (64, 32)
+
+
+@pytest.mark.parametrize("kw,status,match", [
+    (dict(seq_len=0), ra.EINVAL, "seq_len"),
+    (dict(n_shards=0), ra.EINVAL, "n_shards"),
+    (dict(seq_len=1000, n_shards=8), ra.EINVAL, "zig-zag"),
+    (dict(seq_len=1001, split=ra.SPLIT_CONTIGUOUS), ra.EINVAL, "divisible|%|n_shards"),
+    (dict(split=7), ra.EINVAL, "split"),
+    (dict(batch=0), ra.EINVAL, "batch"),
+    (dict(h_q=6, h_kv=4), ra.EINVAL, "h_q"),
+    (dict(h_kv=0), ra.EINVAL, "h_kv"),
+    (dict(head_dim=96), ra.EUNSUPPORTED, "head_dim"),
+    (dict(in_dtype=5), ra.EINVAL, "in_dtype"),
+    (dict(out_dtype=9), ra.EINVAL, "out_dtype"),
+    (dict(in_dtype=ra.F32, out_dtype=ra.BF16), ra.EUNSUPPORTED, "bf16 output"),
+    (dict(causal=2), ra.EINVAL, "causal"),
+    (dict(scale=0.0), ra.EINVAL, "scale"),
+    (dict(scale=float("nan")), ra.EINVAL, "scale"),
+    (dict(seq_len=1 << 31, n_shards=2), ra.EUNSUPPORTED, "2\\^31"),
+])
+def test_descriptor_validation(kw, status, match):
+    expect(status, ra.ring_attn_tile_shape, good_desc(**kw), match=match)
+    kb = [FAKE] * 4
+    expect(status, ra.ring_attn_shard_fwd, good_desc(**kw), 0, FAKE, kb, kb, FAKE, FAKE, match=match)
+
+
+def test_shard_fwd_argument_validation():
+    d = good_desc()
+    kb = [FAKE] * 4
+    expect(ra.EINVAL, ra.ring_attn_shard_fwd, d, 4, FAKE, kb, kb, FAKE, FAKE, match="rank")
+    expect(ra.EINVAL, ra.ring_attn_shard_fwd, d, -1, FAKE, kb, kb, FAKE, FAKE, match="rank")
+    expect(ra.EINVAL, ra.ring_attn_shard_fwd, d, 0, FAKE, [], [], FAKE, FAKE, match="n_blocks")
+    expect(ra.EINVAL, ra.ring_attn_shard_fwd, d, 0, FAKE, [FAKE] * 5, [FAKE] * 5, FAKE, FAKE, match="n_blocks")
+    expect(ra.EINVAL, ra.ring_attn_shard_fwd, d, 0, None, kb, kb, FAKE, FAKE, match="q, out")
+    expect(ra.EINVAL, ra.ring_attn_shard_fwd, d, 0, FAKE, kb, kb, None, FAKE, match="q, out")
+    expect(ra.EINVAL, ra.ring_attn_shard_fwd, d, 0, FAKE, kb, kb, FAKE, None, match="q, out")
+    expect(ra.EINVAL, ra.ring_attn_shard_fwd, d, 0, FAKE + 8, kb, kb, FAKE, FAKE, match="aligned")
+    expect(ra.EINVAL, ra.ring_attn_shard_fwd, d, 0, FAKE, kb, kb, FAKE, FAKE + 2, match="lse")
+    expect(ra.EINVAL, ra.ring_attn_shard_fwd, d, 0, FAKE, kb, kb, FAKE, FAKE, stats=FAKE + 4, match="stats")
+    expect(ra.EINVAL, ra.ring_attn_shard_fwd, d, 0, FAKE, [FAKE, None, FAKE, FAKE], kb, FAKE, FAKE, match="NULL")
+    expect(ra.EINVAL, ra.ring_attn_shard_fwd, d, 0, FAKE, [FAKE, FAKE + 4, FAKE, FAKE], kb, FAKE, FAKE, match="aligned")
+    expect(ra.EINVAL, ra.ring_attn_shard_fwd, d, 0, FAKE, kb[:2], kb[:2], FAKE, FAKE, block_owner=[0, 4], match="block_owner")
+    expect(ra.EINVAL, ra.ring_attn_shard_fwd, d, 0, FAKE, kb[:2], kb[:2], FAKE, FAKE, block_owner=[1, 1], match="repeats")
+    expect(ra.EINVAL, ra.ring_attn_shard_fwd, d, 0, FAKE, kb[:2], kb[:2], FAKE, FAKE, block_owner=[-1, 0], match="block_owner")
+    with pytest.raises(ValueError):
+        ra.ring_attn_shard_fwd(d, 0, FAKE, kb, kb[:3], FAKE, FAKE)
+
+
+def test_too_many_blocks():
+    d = good_desc(seq_len=256 * 200, n_shards=200, split=ra.SPLIT_CONTIGUOUS)
+    kb = [FAKE] * 129
+    expect(ra.EUNSUPPORTED, ra.ring_attn_shard_fwd, d, 0, FAKE, kb, kb, FAKE, FAKE, match="RA_MAX_BLOCKS")
+
+
+def test_partition_validation():
+    expect(ra.EINVAL, ra.zigzag_partition, 1000, 8, ra.SPLIT_ZIGZAG, FAKE, match="zig-zag")
+    expect(ra.EINVAL, ra.zigzag_partition, 1000, 3, ra.SPLIT_CONTIGUOUS, FAKE)
+    expect(ra.EINVAL, ra.zigzag_partition, 0, 1, ra.SPLIT_CONTIGUOUS, FAKE)
+    expect(ra.EINVAL, ra.zigzag_partition, 64, 0, ra.SPLIT_CONTIGUOUS, FAKE)
+    expect(ra.EINVAL, ra.zigzag_partition, 64, 2, 3, FAKE, match="split")
+    expect(ra.EINVAL, ra.zigzag_partition, 64, 2, ra.SPLIT_ZIGZAG, None, match="nothing")
+    expect(ra.EINVAL, ra.zigzag_partition, 64, 2, ra.SPLIT_ZIGZAG, FAKE + 4, match="aligned")
+    expect(ra.EINVAL, ra.zigzag_partition, 64, 2, ra.SPLIT_ZIGZAG, None, FAKE, None, 1, 16, match="both")
+    expect(ra.EINVAL, ra.zigzag_partition, 64, 2, ra.SPLIT_ZIGZAG, None, FAKE, FAKE * 4, 0, 16, match="outer")
+    expect(ra.EINVAL, ra.zigzag_partition, 64, 2, ra.SPLIT_ZIGZAG, None, FAKE, FAKE + 64, 1, 16, match="overlap")
+    expect(ra.EINVAL, ra.zigzag_unpartition, 64, 2, ra.SPLIT_ZIGZAG, None, FAKE, 1, 16, match="set")
+
+
+def test_merge_validation():
+    o, l = [FAKE, FAKE * 2], [FAKE * 3, FAKE * 4]
+    expect(ra.EINVAL, ra.ring_attn_merge, 0, 1, 8, 128, o, ra.F32, l, FAKE * 5, ra.F32, FAKE * 6, match=">= 1")
+    expect(ra.EINVAL, ra.ring_attn_merge, 1, 1, 8, 128, [], ra.F32, [], FAKE * 5, ra.F32, FAKE * 6, match="n_parts")
+    expect(ra.EINVAL, ra.ring_attn_merge, 1, 1, 8, 128, [FAKE] * 65, ra.F32, [FAKE] * 65, FAKE * 5, ra.F32, FAKE * 6, match="n_parts")
+    expect(ra.EUNSUPPORTED, ra.ring_attn_merge, 1, 1, 8, 96, o, ra.F32, l, FAKE * 5, ra.F32, FAKE * 6, match="head_dim")
+    expect(ra.EINVAL, ra.ring_attn_merge, 1, 1, 8, 128, o, 3, l, FAKE * 5, ra.F32, FAKE * 6, match="dtype")
+    expect(ra.EINVAL, ra.ring_attn_merge, 1, 1, 8, 128, [FAKE + 4, FAKE * 2], ra.F32, l, FAKE * 5, ra.F32, FAKE * 6, match="misaligned")
+    expect(ra.EINVAL, ra.ring_attn_merge, 1, 1, 8, 128, o, ra.F32, l, FAKE * 2, ra.F32, FAKE * 6, match="alias")
+    expect(ra.EINVAL, ra.ring_attn_merge, 1, 1, 8, 128, o, ra.BF16, l, FAKE, ra.F32, FAKE * 6, match="in-place")
+    expect(ra.EINVAL, ra.ring_attn_merge, 1, 1, 8, 128, [FAKE, None], ra.F32, l, FAKE * 5, ra.F32, FAKE * 6, match="NULL")
+
+
+def test_last_error_is_thread_local():
+    import threading
+    d = good_desc(batch=0)
+    msgs = {}
+
+    def worker():
+        try:
+            ra.ring_attn_tile_shape(good_desc(head_dim=96))
+        except ra.RingAttnError:
+            pass
+        msgs["t"] = ra.lib().ring_attn_last_error().decode()
+
+    try:
+        ra.ring_attn_tile_shape(d)
+    except ra.RingAttnError:
+        pass
+    th = threading.Thread(target=worker)
+    th.start()
+    th.join()
+    assert "batch" in ra.lib().ring_attn_last_error().decode()
+    assert "head_dim" in msgs["t"]
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(ra, "_lib", None)
+    monkeypatch.setattr(ra, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(ImportError):
+        ra.lib()

@@ -18,7 +18,10 @@ pages name no dataset, so synthetic Gaussians stand in for activations.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
+
 import numpy as np
 
 UNIT = 1024          # positions per independently seeded draw unit
@@ -71,10 +74,25 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     Returns the raw 16-bit patterns as uint16.  Inputs are finite draws.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
-    return r.astype(np.uint16)
+    flat = x.reshape(-1).view(np.uint32)
+    res = np.empty(flat.shape, dtype=np.uint16)
+    step = 1 << 20
+
+    def chunk(lo):
+        u = flat[lo:lo + step].copy()
+        if np.any((u & np.uint32(0x7F800000)) == np.uint32(0x7F800000)):
+            raise ValueError("bf16 rounding expects finite values")
+        # Finite patterns are <= 0xFF7FFFFF, so the sum cannot wrap in 32 bits.
+        t = u >> np.uint32(16)
+        t &= np.uint32(1)
+        t += np.uint32(0x7FFF)
+        u += t
+        u >>= np.uint32(16)
+        res[lo:lo + step] = u
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        list(ex.map(chunk, range(0, flat.size, step)))
+    return res.reshape(x.shape)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -97,7 +115,18 @@ def draw(seed: int, tensor: int, batch: int, heads: int, seq_len: int, head_dim:
     bit patterns of the same draws rounded to nearest even.
     """
     if positions is None:
-        positions = np.arange(seq_len, dtype=np.int64)
+        out = np.empty((batch, heads, seq_len, head_dim), dtype=np.float32)
+        jobs = [(b, h, u) for b in range(batch) for h in range(heads) for u in range(-(-seq_len // UNIT))]
+
+        def fill(job):
+            b, h, u = job
+            lo = u * UNIT
+            n = min(UNIT, seq_len - lo)
+            out[b, h, lo:lo + n] = _unit_draw(seed, tensor, b, h, u, n, head_dim)
+
+        with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+            list(ex.map(fill, jobs))
+        return _finish(out, sigma, dtype)
     positions = np.asarray(positions, dtype=np.int64)
     if positions.size and (positions.min() < 0 or positions.max() >= seq_len):
         raise ValueError("position out of range")
@@ -111,6 +140,10 @@ def draw(seed: int, tensor: int, batch: int, heads: int, seq_len: int, head_dim:
                 vals = _unit_draw(seed, tensor, b, h, int(u), n, head_dim)
                 sel = np.nonzero(units == u)[0]
                 out[b, h, sel, :] = vals[positions[sel] - lo]
+    return _finish(out, sigma, dtype)
+
+
+def _finish(out: np.ndarray, sigma: float, dtype: str) -> np.ndarray:
     if sigma != 1.0:
         out *= np.float32(sigma)
     if dtype == "f32":
