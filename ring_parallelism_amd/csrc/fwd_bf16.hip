@@ -5,31 +5,37 @@
 // (running max, normaliser, rescale when the max rises; "Sequence / context
 // parallelism" notes, section 4; "Sequence Parallelism and Ring Attention
 // Quiz", Q3 and Q7).  Blocks that would arrive over the ring are streamed
-// HBM -> registers -> LDS, the next tile's loads in flight while the current
-// tile is computed (double-buffered LDS).  The causal mask is resolved per
-// (block, tile) from token positions: tiles entirely after the query tile are
-// never loaded, tiles entirely before it run unmasked, and only the few
-// tiles that straddle the diagonal apply an elementwise mask.
+// HBM -> LDS by the buffer unit's LDS-direct loads (no register staging),
+// the next tile in flight while the current one is computed (double-buffered
+// LDS).  The causal mask is resolved per (block, tile) from token positions:
+// tiles entirely after the query tile are never loaded, tiles entirely before
+// it run unmasked, and only tiles that straddle the diagonal (or the shard
+// end) apply an elementwise mask.
 //
 // Matrix-core formulation (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
-//   S^T = K Q^T : A = a 32-key slice of K (LDS), B = Q^T (registers).  Each
-//                 lane then owns one query column and 16 of its scores, so a
-//                 row max is an in-lane max plus one permlane32 swap.
-//   O^T += V^T P^T : A = V^T (LDS, stored transposed), B = P^T straight from
-//                 the score registers after the exp and a bf16 cast; the key
-//                 order inside each 16-key step is the accumulator's own row
-//                 order, matched on the V^T side.
+//   S^T = K Q^T    A = a 32-key slice of K (LDS, ds_read_b128), B = Q^T
+//                  (registers for the whole pass).  Each lane then owns one
+//                  query column and 16 of its scores, so a row max is an
+//                  in-lane max plus one permlane32 swap.
+//   O^T += V^T P^T A = V^T, read from the row-major V tile with the
+//                  transposing LDS read (ds_read_b64_tr_b16); B = P^T taken
+//                  straight from the score registers after exp2 and a bf16
+//                  cast.  The key order inside each 16-key step is the score
+//                  accumulator's row order, matched on the V side.
+// LDS tiles are stored with an XOR swizzle of their 16-byte chunks so both
+// the ds_read_b128 of K and the transposing reads of V hit distinct banks.
+//
 // The softmax works in the log2 domain (scale * log2 e folded into one fma
 // before v_exp_f32).  The reference max only moves when a tile's max exceeds
 // it by more than 8 (log2 units), so exp2 arguments stay <= 8 and the output
-// rescale runs on a few tiles per row instead of every tile; the result is
-// the same up to rounding because l and O use the same reference.
+// rescale runs on a few tiles per row instead of every tile; l and O share
+// the reference, so the result is the same up to rounding.
 //
 // Workgroup: NW wavefronts x NB 32-row blocks = BQ query rows of one
 // (batch, head).  Each workgroup takes query tiles p and n_qtiles-1-p of the
 // shard: under a causal mask their visible key counts add to a constant for
-// both contiguous and zig-zag placement, so every workgroup does the same work
-// (the zig-zag balancing idea applied to tiles inside one shard).
+// contiguous, zig-zag and striped placement alike, so every workgroup does the
+// same work (the zig-zag balancing idea applied to tiles inside one shard).
 // Consecutive workgroup ids are placed on one XCD, so the query heads that
 // share a key/value head stream the same K/V through one L2.
 #include "ra_common.h"
@@ -40,9 +46,12 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr float kRescaleThreshold = 8.0f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kBK = 64;                 // keys per tile
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
 
 // Combine a value across the two half-waves (lanes l and l ^ 32).  The swap
 // returns the pair {own, partner} (in an order that depends on the half), so
@@ -57,34 +66,45 @@ __device__ inline float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ inline uint32_t word_of(const uint4& v, int i) {
-  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+// 16 bytes per lane from a buffer resource straight into LDS: lane i's data
+// lands at dst + 16 * i (dst is wave-uniform); out-of-range offsets read 0.
+// Kept as a plain device function: the host pass of a kernel template that
+// names this builtin directly emits no launch stub.
+__device__ inline void lds_load16(__amdgpu_buffer_rsrc_t r, lds_char* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
 }
 
-template <int D, int NW, int NB, int BK>
+template <int D, int NW, int NB>
 struct Cfg {
-  static constexpr int NT = NW * 64;        // threads
-  static constexpr int BQ = NW * NB * 32;   // query rows per tile
-  static constexpr int KSTR = D + 8;        // K row stride (bf16): +16 B keeps ds_read_b128 conflict-free
-  static constexpr int VSTR = BK + 4;       // V^T row stride (bf16): +8 B keeps ds_read_b64 conflict-free
-  static constexpr int KTILE = BK * KSTR;
-  static constexpr int VTILE = D * VSTR;
-  static constexpr int STAGE = KTILE + VTILE;
-  static constexpr int KCH = BK * (D / 8) / NT;   // 16-byte K chunks per thread per tile
-  static constexpr int VKPT = BK * (D / 8) / NT;  // keys per thread in the V transpose
-  static constexpr int VKG = BK / VKPT;           // key groups
-  static_assert(BK == 64, "two 32-key MFMA blocks per tile");
-  static_assert(KCH >= 1 && BK * (D / 8) % NT == 0, "tile must split evenly over threads");
-  static_assert(VKPT == 2 || VKPT == 4, "V transpose packs 2 or 4 keys");
+  static constexpr int NT = NW * 64;
+  static constexpr int BQ = NW * NB * 32;
+  static constexpr int ROWB = D * 2;                  // bytes per K / V row
+  static constexpr int CHUNKS = ROWB / 16;            // 16-byte chunks per row
+  static constexpr int TILEB = kBK * ROWB;            // bytes per K or V tile
+  static constexpr int STAGEB = 2 * TILEB;            // K tile then V tile
+  static constexpr int RPI = 1024 / ROWB;             // rows per 64-lane 16-byte load
+  static constexpr int LOADS = TILEB / 1024 / NW;     // loads per wave per tile, each tensor
+  static_assert(LOADS >= 1 && TILEB % (1024 * NW) == 0, "tile must split evenly over waves");
+  static_assert(D == 64 || D == 128, "head_dim");
+
+  // 16-byte slot holding chunk c of tile row r (an involution in c).
+  // K: rows r..r+15 read at one chunk land in 16 different slots.
+  __device__ static int k_slot(int r, int c) { return c ^ (r & (CHUNKS - 1)); }
+  // V: the transposing reads of a half-wave touch rows r..r+3 (4 chunks each
+  // for d = 128); moving each row's chunk group keeps them apart.
+  __device__ static int v_slot(int r, int c) {
+    return D == 128 ? c ^ ((r & 3) << 2) : c ^ (((r >> 1) & 1) << 2);
+  }
 };
 
-template <int D, int NW, int NB, int BK, typename OutT>
+template <int D, int NW, int NB, typename OutT>
 __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
-  using C = Cfg<D, NW, NB, BK>;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * C::STAGE];
+  using C = Cfg<D, NW, NB>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGEB];
+  lds_char* const lds = (lds_char*)smem;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int lc = lane & 31;  // query column inside a 32-block
   const int g = lane >> 5;   // half-wave
@@ -102,10 +122,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
   const int n_loc = (int)p.n_loc;
   const int64_t kv_off = ((int64_t)b * p.h_kv + hk) * n_loc * D;
   const int64_t q_off = ((int64_t)b * p.h_q + h) * n_loc;
+  const int kv_bytes = n_loc * C::ROWB;  // one (batch, kv head) slice of a block
 
-  // Loader thread roles.
-  const int v_kg = tid % C::VKG;  // key group of the V transpose
-  const int v_dc = tid / C::VKG;  // 8-wide d chunk of the V transpose
+  // LDS-direct load roles: lane -> (row in its 1 KiB group, 16-byte slot).
+  const int ld_row = lane / C::CHUNKS;
+  const int ld_slot = lane % C::CHUNKS;
+
+  // Transposing-read roles for V: 16-lane group qg, lane jj inside it.
+  const int qg = lane >> 4, jj = lane & 15;
+  const int v_row = 4 * g + (jj >> 2);           // + 16 * step (+ 8 for the high half)
+  const int v_d = 16 * (qg & 1) + 4 * (jj & 3);  // + 32 * d-block
 
   uint32_t pairs_partial = 0;  // per lane, masked tiles only
 
@@ -127,15 +153,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
     for (int nb = 0; nb < NB; ++nb) {
       const int row = i0 + (wave * NB + nb) * 32 + lc;
       const bool ok = row < n_loc;
-      // Rows past the shard end get -2: below every key "position" the mask
-      // uses (-1 marks any valid key when the mask is not causal).
-      posq[nb] = ok ? token_pos32(p.rank, row, n_loc, p.c, p.split) : -2;
+      posq[nb] = ok ? token_pos32(p.rank, row, n_loc, p.c, p.split) : -1;  // -1: past the shard end
       const __bf16* qp = (const __bf16*)p.q + (q_off + (ok ? row : 0)) * D + g * 8;
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) qreg[nb][s] = ok ? *(const bf16x8*)(qp + s * 16) : bf16x8{};
     }
 
-    // Online-softmax state, one query row per lane per 32-block.
     f32x16 oacc[D / 32][NB];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -153,8 +176,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       const int j = p.owner[t];
       const int c_last = p.causal ? count_upto32(j, pos_last, n_loc, p.c, p.split) : n_loc;
       const int c_first = p.causal ? count_upto32(j, pos_first, n_loc, p.c, p.split) : n_loc;
-      n_vis = (c_last + BK - 1) / BK;
-      n_full = rows_full ? c_first / BK : 0;
+      n_vis = (c_last + kBK - 1) / kBK;
+      n_full = rows_full ? c_first / kBK : 0;
     };
     auto next_block = [&](int& t, int& kt, int& n_vis, int& n_full) {
       ++t;
@@ -168,68 +191,39 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
     int cur_t = -1, cur_kt = 0, cur_vis = 0, cur_full = 0;
     next_block(cur_t, cur_kt, cur_vis, cur_full);
 
-    uint4 kreg[C::KCH], vreg[C::VKPT];
-    auto load_regs = [&](int t, int kt) {
-      const __bf16* kp = (const __bf16*)p.k[t] + kv_off;
-      const __bf16* vp = (const __bf16*)p.v[t] + kv_off;
-      const int key0 = kt * BK;
+    // Put tile (t, kt)'s K and V into LDS stage `st`.  Rows past the shard
+    // end fall outside the buffer resource and read as zeros.
+    auto issue_loads = [&](int st, int t, int kt) {
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)((const __bf16*)p.k[t] + kv_off), (short)0, kv_bytes, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)((const __bf16*)p.v[t] + kv_off), (short)0, kv_bytes, kRsrcWord3);
+      lds_char* kdst = lds + st * C::STAGEB;
+      lds_char* vdst = kdst + C::TILEB;
 #pragma unroll
-      for (int u = 0; u < C::KCH; ++u) {
-        const int cid = tid + C::NT * u;
-        const int key = key0 + cid / (D / 8), ch = cid % (D / 8);
-        kreg[u] = key < n_loc ? *(const uint4*)(kp + key * D + ch * 8) : uint4{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int u = 0; u < C::VKPT; ++u) {
-        const int key = key0 + v_kg * C::VKPT + u;
-        vreg[u] = key < n_loc ? *(const uint4*)(vp + key * D + v_dc * 8) : uint4{0, 0, 0, 0};
-      }
-    };
-    auto store_lds = [&](int buf) {
-      __bf16* ks = smem + buf * C::STAGE;
-      __bf16* vt = ks + C::KTILE;
-#pragma unroll
-      for (int u = 0; u < C::KCH; ++u) {
-        const int cid = tid + C::NT * u;
-        const int kk = cid / (D / 8), ch = cid % (D / 8);
-        *(uint4*)(ks + kk * C::KSTR + ch * 8) = kreg[u];
-      }
-      // Transpose: element e of the 8-wide d chunk goes to row v_dc*8+e of V^T.
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) * 16;
-        uint32_t pk[C::VKPT / 2];
-#pragma unroll
-        for (int u2 = 0; u2 < C::VKPT / 2; ++u2) {
-          const uint32_t a = (word_of(vreg[2 * u2], e / 2) >> sh) & 0xffffu;
-          const uint32_t c = (word_of(vreg[2 * u2 + 1], e / 2) >> sh) & 0xffffu;
-          pk[u2] = a | (c << 16);
-        }
-        __bf16* dst = vt + (v_dc * 8 + e) * C::VSTR + v_kg * C::VKPT;
-        if constexpr (C::VKPT == 4) {
-          *(uint2*)dst = uint2{pk[0], pk[1]};
-        } else {
-          *(uint32_t*)dst = pk[0];
-        }
+      for (int u = 0; u < C::LOADS; ++u) {
+        const int grp = wave * C::LOADS + u;  // 1 KiB group of the tile
+        const int row = grp * C::RPI + ld_row;
+        const uint32_t rowoff = (uint32_t)(kt * kBK + row) * C::ROWB;
+        lds_load16(rk, kdst + grp * 1024, rowoff + C::k_slot(row, ld_slot) * 16);
+        lds_load16(rv, vdst + grp * 1024, rowoff + C::v_slot(row, ld_slot) * 16);
       }
     };
 
-    if (cur_t < p.n_blocks) {
-      load_regs(cur_t, cur_kt);
-      store_lds(0);
-    }
+    if (cur_t < p.n_blocks) issue_loads(0, cur_t, cur_kt);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    int buf = 0;
+    int st = 0;
 
     while (cur_t < p.n_blocks) {
       // Advance a copy of the iterator and put the next tile's loads in flight.
       int nt = cur_t, nkt = cur_kt + 1, nvis = cur_vis, nfull = cur_full;
       if (nkt >= nvis) next_block(nt, nkt, nvis, nfull);
       const bool has_next = nt < p.n_blocks;
-      if (has_next) load_regs(nt, nkt);
+      if (has_next) issue_loads(st ^ 1, nt, nkt);
 
-      const __bf16* ks = smem + buf * C::STAGE;
-      const __bf16* vt = ks + C::KTILE;
+      const lds_char* ks = lds + st * C::STAGEB;
+      const lds_char* vs = ks + C::TILEB;
 
       // S^T = K Q^T for the tile's two 32-key blocks.
       f32x16 sacc[2][NB];
@@ -241,7 +235,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       for (int s = 0; s < D / 16; ++s) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          const bf16x8 a = *(const bf16x8*)(ks + (mb * 32 + lc) * C::KSTR + s * 16 + g * 8);
+          const int row = mb * 32 + lc;
+          const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(
+              ks + row * C::ROWB + C::k_slot(row, 2 * s + g) * 16);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
             sacc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[nb][s], sacc[mb][nb], 0, 0, 0);
@@ -249,23 +245,28 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       }
 
       // Elementwise mask on tiles that straddle the diagonal or the shard end.
+      // Key positions ascend inside a block, so the keys a query sees there
+      // are the block's first count_upto(j, pos_q) rows: one bound per row.
       // Accumulator element i of block mb is key mb*32 + (i/4)*8 + g*4 + i%4.
       if (cur_kt >= cur_full) {
         const int j = p.owner[cur_t];
-        const int key0 = cur_kt * BK + g * 4;
+        int lim[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int cnt = posq[nb] < 0 ? 0
+                          : (p.causal ? count_upto32(j, posq[nb], n_loc, p.c, p.split) : n_loc);
+          lim[nb] = cnt - cur_kt * kBK - g * 4;
+        }
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int jj = key0 + mb * 32 + (i / 4) * 8 + (i % 4);
-            // Keys past the shard end get a position no query reaches.
-            const int pk = jj < n_loc ? (p.causal ? token_pos32(j, jj, n_loc, p.c, p.split) : -1)
-                                      : 0x7fffffff;
+            const int off = mb * 32 + (i / 4) * 8 + (i % 4);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-              const bool vis = pk <= posq[nb];
+              const bool vis = off < lim[nb];
               pairs_partial += vis ? 1u : 0u;
-              if (!vis) sacc[mb][nb][i] = -INFINITY;
+              sacc[mb][nb][i] = vis ? sacc[mb][nb][i] : -INFINITY;
             }
           }
       }
@@ -303,15 +304,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int half = 0; half < 2; ++half) {
+          for (int hh = 0; hh < 2; ++hh) {
             bf16x8 v8;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][nb][half * 8 + e], p.scale_log2, -msub));
+              const float pe = __builtin_amdgcn_exp2f(
+                  __builtin_fmaf(sacc[mb][nb][hh * 8 + e], p.scale_log2, -msub));
               ls += pe;
               v8[e] = (__bf16)pe;
             }
-            pb[nb][mb * 2 + half] = v8;
+            pb[nb][mb * 2 + hh] = v8;
           }
         l_part[nb] += ls;
       }
@@ -320,21 +322,27 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
-        for (int ks16 = 0; ks16 < 4; ++ks16) {
-          const int kb = (ks16 >> 1) * 32 + (ks16 & 1) * 16 + g * 4;
-          const __bf16* vr = vt + (db * 32 + lc) * C::VSTR + kb;
-          const bf16x4 lo = *(const bf16x4*)(vr);
-          const bf16x4 hi = *(const bf16x4*)(vr + 8);
+        for (int k16 = 0; k16 < 4; ++k16) {
+          const int row = k16 * 16 + v_row;
+          const int d = db * 32 + v_d;
+          const int off = row * C::ROWB + C::v_slot(row, d >> 3) * 16 + (d & 7) * 2;
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4*)(vs + off));
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4*)(vs + off + 8 * C::ROWB));
           const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
-            oacc[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[nb][ks16], oacc[db][nb], 0, 0, 0);
+            oacc[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[nb][k16], oacc[db][nb], 0, 0, 0);
         }
       }
 
-      if (has_next) store_lds(buf ^ 1);
+      // The next tile's LDS-direct loads must have landed before anyone
+      // reads that stage, and this stage must be drained before it is
+      // refilled: one wait and one barrier per tile.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      buf ^= 1;
+      st ^= 1;
       cur_t = nt;
       cur_kt = nkt;
       cur_vis = nvis;
@@ -391,12 +399,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
         const int j = p.owner[t];
         const int c_last = p.causal ? count_upto32(j, pos_last, n_loc, p.c, p.split) : n_loc;
         const int c_first = p.causal ? count_upto32(j, pos_first, n_loc, p.c, p.split) : n_loc;
-        const int n_vis = (c_last + BK - 1) / BK;
-        const int n_full = rows_full ? c_first / BK : 0;
+        const int n_vis = (c_last + kBK - 1) / kBK;
+        const int n_full = rows_full ? c_first / kBK : 0;
         t_full += n_full;
         t_part += n_vis - n_full;
         t_skip += p.n_ktiles - n_vis;
-        pairs_full += (unsigned long long)n_full * C::BQ * BK;
+        pairs_full += (unsigned long long)n_full * C::BQ * kBK;
       }
     }
     unsigned long long v = pairs_partial;
@@ -412,15 +420,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-constexpr int kNW = 4, kNB = 1, kBK = 64;
+constexpr int kNW = 4, kNB = 2;
 
 template <int D, typename OutT>
 hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
-  using C = Cfg<D, kNW, kNB, kBK>;
+  using C = Cfg<D, kNW, kNB>;
   const int64_t grid = (int64_t)p.batch * p.h_q * p.n_pairs;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, kNW, kNB, kBK, OutT>), dim3((unsigned)grid), dim3(C::NT),
-                     0, stream, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, kNW, kNB, OutT>), dim3((unsigned)grid), dim3(C::NT), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
