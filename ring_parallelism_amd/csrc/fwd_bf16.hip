@@ -38,6 +38,8 @@
 // same work (the zig-zag balancing idea applied to tiles inside one shard).
 // Consecutive workgroup ids are placed on one XCD, so the query heads that
 // share a key/value head stream the same K/V through one L2.
+#include <type_traits>
+
 #include "ra_common.h"
 
 namespace ra {
@@ -50,7 +52,6 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr float kRescaleThreshold = 8.0f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kBK = 64;                 // keys per tile
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
 
 // Combine a value across the two half-waves (lanes l and l ^ 32).  The swap
@@ -74,14 +75,16 @@ __device__ inline void lds_load16(__amdgpu_buffer_rsrc_t r, lds_char* dst, uint3
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
 }
 
-template <int D, int NW, int NB>
+template <int D, int NW, int NB, int MB>
 struct Cfg {
   static constexpr int NT = NW * 64;
   static constexpr int BQ = NW * NB * 32;
+  static constexpr int BK = MB * 32;                  // keys per tile (MB 32-key MFMA blocks)
   static constexpr int ROWB = D * 2;                  // bytes per K / V row
   static constexpr int CHUNKS = ROWB / 16;            // 16-byte chunks per row
-  static constexpr int TILEB = kBK * ROWB;            // bytes per K or V tile
+  static constexpr int TILEB = BK * ROWB;             // bytes per K or V tile
   static constexpr int STAGEB = 2 * TILEB;            // K tile then V tile
+  static constexpr int STAGES = 3;
   static constexpr int RPI = 1024 / ROWB;             // rows per 64-lane 16-byte load
   static constexpr int LOADS = TILEB / 1024 / NW;     // loads per wave per tile, each tensor
   static_assert(LOADS >= 1 && TILEB % (1024 * NW) == 0, "tile must split evenly over waves");
@@ -97,11 +100,20 @@ struct Cfg {
   }
 };
 
-template <int D, int NW, int NB, typename OutT>
+template <int D, int NW, int NB, int MB, typename OutT>
 __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
-  using C = Cfg<D, NW, NB>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGEB];
-  lds_char* const lds = (lds_char*)smem;
+  using C = Cfg<D, NW, NB, MB>;
+  constexpr int kBK = C::BK;
+  // Three LDS stages as separate objects: the compiler then knows that the
+  // LDS-direct loads filling one stage cannot alias reads of another, and does
+  // not make those reads wait for the loads in flight.
+  __shared__ __attribute__((aligned(1024))) char smem0[C::STAGEB];
+  __shared__ __attribute__((aligned(1024))) char smem1[C::STAGEB];
+  __shared__ __attribute__((aligned(1024))) char smem2[C::STAGEB];
+  auto stage = [&](auto S) -> lds_char* {
+    constexpr int st = decltype(S)::value;
+    return st == 0 ? (lds_char*)smem0 : (st == 1 ? (lds_char*)smem1 : (lds_char*)smem2);
+  };
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -171,70 +183,58 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       l_part[nb] = 0.f;
     }
 
-    // Tile iterator over (block t, key tile kt), skipping blocks with no visible key.
-    auto block_counts = [&](int t, int& n_vis, int& n_full) {
-      const int j = p.owner[t];
+    // Tile iterator over (block t, key tile kt), skipping blocks with no
+    // visible key.  A state is (t, kt, n_vis, n_full); t >= n_blocks: done.
+    struct Tile {
+      int t, kt, vis, full;
+    };
+    auto block_counts = [&](Tile& x) {
+      const int j = p.owner[x.t];
       const int c_last = p.causal ? count_upto32(j, pos_last, n_loc, p.c, p.split) : n_loc;
       const int c_first = p.causal ? count_upto32(j, pos_first, n_loc, p.c, p.split) : n_loc;
-      n_vis = (c_last + kBK - 1) / kBK;
-      n_full = rows_full ? c_first / kBK : 0;
+      x.vis = (c_last + kBK - 1) / kBK;
+      x.full = rows_full ? c_first / kBK : 0;
     };
-    auto next_block = [&](int& t, int& kt, int& n_vis, int& n_full) {
-      ++t;
-      while (t < p.n_blocks) {
-        block_counts(t, n_vis, n_full);
-        if (n_vis > 0) break;
-        ++t;
+    auto advance = [&](Tile x) {
+      if (x.t >= p.n_blocks) return x;
+      if (++x.kt < x.vis) return x;
+      x.kt = 0;
+      while (++x.t < p.n_blocks) {
+        block_counts(x);
+        if (x.vis > 0) break;
       }
-      kt = 0;
+      return x;
     };
-    int cur_t = -1, cur_kt = 0, cur_vis = 0, cur_full = 0;
-    next_block(cur_t, cur_kt, cur_vis, cur_full);
+    auto valid = [&](const Tile& x) { return x.t < p.n_blocks; };
 
-    // Put tile (t, kt)'s K and V into LDS stage `st`.  Rows past the shard
-    // end fall outside the buffer resource and read as zeros.
-    auto issue_loads = [&](int st, int t, int kt) {
+    // Put tile x's K and V into LDS stage `st`.  Rows past the shard end fall
+    // outside the buffer resource and read as zeros.
+    auto issue_loads = [&](lds_char* kdst, const Tile& x) {
       const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)((const __bf16*)p.k[t] + kv_off), (short)0, kv_bytes, kRsrcWord3);
+          (void*)((const __bf16*)p.k[x.t] + kv_off), (short)0, kv_bytes, kRsrcWord3);
       const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)((const __bf16*)p.v[t] + kv_off), (short)0, kv_bytes, kRsrcWord3);
-      lds_char* kdst = lds + st * C::STAGEB;
+          (void*)((const __bf16*)p.v[x.t] + kv_off), (short)0, kv_bytes, kRsrcWord3);
       lds_char* vdst = kdst + C::TILEB;
 #pragma unroll
       for (int u = 0; u < C::LOADS; ++u) {
         const int grp = wave * C::LOADS + u;  // 1 KiB group of the tile
         const int row = grp * C::RPI + ld_row;
-        const uint32_t rowoff = (uint32_t)(kt * kBK + row) * C::ROWB;
+        const uint32_t rowoff = (uint32_t)(x.kt * kBK + row) * C::ROWB;
         lds_load16(rk, kdst + grp * 1024, rowoff + C::k_slot(row, ld_slot) * 16);
         lds_load16(rv, vdst + grp * 1024, rowoff + C::v_slot(row, ld_slot) * 16);
       }
     };
 
-    if (cur_t < p.n_blocks) issue_loads(0, cur_t, cur_kt);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    int st = 0;
-
-    while (cur_t < p.n_blocks) {
-      // Advance a copy of the iterator and put the next tile's loads in flight.
-      int nt = cur_t, nkt = cur_kt + 1, nvis = cur_vis, nfull = cur_full;
-      if (nkt >= nvis) next_block(nt, nkt, nvis, nfull);
-      const bool has_next = nt < p.n_blocks;
-      if (has_next) issue_loads(st ^ 1, nt, nkt);
-
-      const lds_char* ks = lds + st * C::STAGEB;
-      const lds_char* vs = ks + C::TILEB;
-
-      // S^T = K Q^T for the tile's two 32-key blocks.
-      f32x16 sacc[2][NB];
+    // S^T = K Q^T for the tile in stage st (two 32-key blocks).
+    auto qk = [&](f32x16 (&sacc)[MB][NB], const lds_char* ks) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) sacc[mb][nb] = f32x16{};
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
           const int row = mb * 32 + lc;
           const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(
               ks + row * C::ROWB + C::k_slot(row, 2 * s + g) * 16);
@@ -243,73 +243,95 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
             sacc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[nb][s], sacc[mb][nb], 0, 0, 0);
         }
       }
+    };
 
-      // Elementwise mask on tiles that straddle the diagonal or the shard end.
-      // Key positions ascend inside a block, so the keys a query sees there
-      // are the block's first count_upto(j, pos_q) rows: one bound per row.
-      // Accumulator element i of block mb is key mb*32 + (i/4)*8 + g*4 + i%4.
-      if (cur_kt >= cur_full) {
-        const int j = p.owner[cur_t];
-        int lim[NB];
+    // Elementwise mask on a tile that straddles the diagonal or the shard
+    // end.  Key positions ascend inside a block, so the keys a query sees
+    // there are the block's first count_upto(j, pos_q) rows: one bound per
+    // row.  Accumulator element i of block mb is key mb*32 + (i/4)*8 + g*4 + i%4.
+    auto mask = [&](f32x16 (&sacc)[MB][NB], const Tile& x) {
+      const int j = p.owner[x.t];
+      int lim[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int cnt = posq[nb] < 0 ? 0
-                          : (p.causal ? count_upto32(j, posq[nb], n_loc, p.c, p.split) : n_loc);
-          lim[nb] = cnt - cur_kt * kBK - g * 4;
-        }
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int off = mb * 32 + (i / 4) * 8 + (i % 4);
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-              const bool vis = off < lim[nb];
-              pairs_partial += vis ? 1u : 0u;
-              sacc[mb][nb][i] = vis ? sacc[mb][nb][i] : -INFINITY;
-            }
-          }
+      for (int nb = 0; nb < NB; ++nb) {
+        const int cnt = posq[nb] < 0 ? 0
+                        : (p.causal ? count_upto32(j, posq[nb], n_loc, p.c, p.split) : n_loc);
+        lim[nb] = cnt - x.kt * kBK - g * 4;
       }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int off = mb * 32 + (i / 4) * 8 + (i % 4);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const bool vis = off < lim[nb];
+            pairs_partial += vis ? 1u : 0u;
+            sacc[mb][nb][i] = vis ? sacc[mb][nb][i] : -INFINITY;
+          }
+        }
+    };
 
-      // Online softmax (log2 domain).
-      float mt[NB];
-      bool need = false;
+    // Tile max of the scaled scores (log2 units), both half-waves combined.
+    auto row_max = [&](const f32x16 (&sacc)[MB][NB], float (&mt)[NB]) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         float mx = -INFINITY;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mb][nb][i]);
-        mx = halves_max(mx);
-        mt[nb] = mx * p.scale_log2;
-        need |= mt[nb] > m_ref[nb] + kRescaleThreshold;
+        mt[nb] = halves_max(mx) * p.scale_log2;
       }
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const float m_new = fmaxf(m_ref[nb], mt[nb]);
-          const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref[nb] - m_new);
-          l_part[nb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) oacc[db][nb] *= alpha;
-          m_ref[nb] = m_new;
-        }
-      }
-      bf16x8 pb[NB][4];
+    };
+
+    // x = scale*log2(e)*s - m_ref, in place (m_ref = -inf: shift by 0).
+    auto shift = [&](f32x16 (&sacc)[MB][NB]) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const float msub = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sacc[mb][nb][i] = __builtin_fmaf(sacc[mb][nb][i], p.scale_log2, -msub);
+      }
+    };
+
+    // Raise the reference max where a tile's max exceeds it by more than the
+    // threshold: rescale O and l, and re-shift the pending tile's x values.
+    auto rescale = [&](const float (&mt)[NB], f32x16 (&xnext)[MB][NB]) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const float m_new = fmaxf(m_ref[nb], mt[nb]);
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref[nb] - m_new);
+        const float old_sub = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
+        const float new_sub = (m_new == -INFINITY) ? 0.f : m_new;
+        const float dx = old_sub - new_sub;
+        l_part[nb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db][nb] *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) xnext[mb][nb][i] += dx;
+        m_ref[nb] = m_new;
+      }
+    };
+
+    // P = bf16(exp2(x)) as the B operand of the value product; l gathers
+    // the fp32 sum (the log-sum-exp needs it unrounded).
+    auto exps = [&](const f32x16 (&x)[MB][NB], bf16x8 (&pb)[NB][2 * MB]) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
         float ls = 0.f;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             bf16x8 v8;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const float pe = __builtin_amdgcn_exp2f(
-                  __builtin_fmaf(sacc[mb][nb][hh * 8 + e], p.scale_log2, -msub));
+              const float pe = __builtin_amdgcn_exp2f(x[mb][nb][hh * 8 + e]);
               ls += pe;
               v8[e] = (__bf16)pe;
             }
@@ -317,12 +339,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
           }
         l_part[nb] += ls;
       }
+    };
 
-      // O^T += V^T P^T, 16 keys per MFMA step.
+    // O^T += V^T P^T for the tile in stage st, 16 keys per MFMA step.
+    auto pv = [&](const lds_char* stage_base, const bf16x8 (&pb)[NB][2 * MB]) {
+      const lds_char* vs = stage_base + C::TILEB;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
-        for (int k16 = 0; k16 < 4; ++k16) {
+        for (int k16 = 0; k16 < 2 * MB; ++k16) {
           const int row = k16 * 16 + v_row;
           const int d = db * 32 + v_d;
           const int off = row * C::ROWB + C::v_slot(row, d >> 3) * 16 + (d & 7) * 2;
@@ -336,17 +361,84 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
             oacc[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[nb][k16], oacc[db][nb], 0, 0, 0);
         }
       }
+    };
 
-      // The next tile's LDS-direct loads must have landed before anyone
-      // reads that stage, and this stage must be drained before it is
-      // refilled: one wait and one barrier per tile.
+    // Software pipeline over the tile sequence, three LDS stages in a ring.
+    // Step i: loads of tile i+2 in flight; the scores of tile i+1 (matrix
+    // cores) run beside the exponentials of tile i (vector unit); then the
+    // value product of tile i runs beside the max and shift of tile i+1.
+    Tile t0;
+    t0.t = -1;
+    t0.kt = 0;
+    t0.vis = 0;
+    t0.full = 0;
+    while (++t0.t < p.n_blocks) {
+      block_counts(t0);
+      if (t0.vis > 0) break;
+    }
+    Tile t1 = advance(t0), t2 = advance(t1);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    if (valid(t0)) issue_loads(stage(I0{}), t0);
+    if (valid(t1)) issue_loads(stage(I1{}), t1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    f32x16 xa[MB][NB], xb[MB][NB];
+    bf16x8 pb[NB][2 * MB];
+    float mt[NB];
+    if (valid(t0)) {
+      qk(xa, stage(I0{}));
+      if (t0.kt >= t0.full) mask(xa, t0);
+      row_max(xa, mt);
+      shift(xa);
+      rescale(mt, xa);  // first reference max (O and l are still zero)
+    }
+
+    // One pipeline step; S0, S1, S2 are the (compile-time) stages of tiles
+    // i, i+1, i+2.  Returns false once tile i+1 is past the end.
+    auto step = [&](auto S0, auto S1, auto S2, f32x16 (&x)[MB][NB], f32x16 (&y)[MB][NB]) {
+      if (valid(t2)) issue_loads(stage(S2), t2);
+      qk(y, stage(S1));  // harmless when t1 is past the end: its result is unused
+      exps(x, pb);
+      // Materialise P here, beside the score products, rather than after the
+      // (rare) mask branch below.
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int k4 = 0; k4 < 2 * MB; ++k4) asm volatile("" : "+v"(pb[nb][k4]));
+      if (valid(t1) && t1.kt >= t1.full) mask(y, t1);
+      pv(stage(S0), pb);
+      row_max(y, mt);
+      bool need = false;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) need |= mt[nb] > m_ref[nb] + kRescaleThreshold;
+      need = need && valid(t1);
+      shift(y);
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        // Rare path: keep it a real branch (if-converting it would put the
+        // whole output rescale on every tile).
+        asm volatile("" ::: "memory");
+        rescale(mt, y);
+      }
+      // Tile i+2 must have landed before the next step reads it, and stage
+      // S0 must be drained before the next step refills it.
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      st ^= 1;
-      cur_t = nt;
-      cur_kt = nkt;
-      cur_vis = nvis;
-      cur_full = nfull;
+      t0 = t1;
+      t1 = t2;
+      t2 = advance(t2);
+      return valid(t0);
+    };
+    // Stages rotate with period 3 and the score buffers with period 2.
+    while (valid(t0)) {
+      if (!step(I0{}, I1{}, I2{}, xa, xb)) break;
+      if (!step(I1{}, I2{}, I0{}, xb, xa)) break;
+      if (!step(I2{}, I0{}, I1{}, xa, xb)) break;
+      if (!step(I0{}, I1{}, I2{}, xb, xa)) break;
+      if (!step(I1{}, I2{}, I0{}, xa, xb)) break;
+      if (!step(I2{}, I0{}, I1{}, xb, xa)) break;
     }
 
     // Epilogue: out = O / l, lse = ln 2 * (m_ref + log2 l).
@@ -420,15 +512,26 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-constexpr int kNW = 4, kNB = 2;
+// Tile configuration: waves per workgroup, 32-row query blocks per wave,
+// 32-key blocks per pipeline step.  (Compile-time knobs for tuning sweeps.)
+#ifndef RA_FWD_NW
+#define RA_FWD_NW 4
+#endif
+#ifndef RA_FWD_NB
+#define RA_FWD_NB 2
+#endif
+#ifndef RA_FWD_MB
+#define RA_FWD_MB 1
+#endif
+constexpr int kNW = RA_FWD_NW, kNB = RA_FWD_NB, kMB = RA_FWD_MB;
 
 template <int D, typename OutT>
 hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
-  using C = Cfg<D, kNW, kNB>;
+  using C = Cfg<D, kNW, kNB, kMB>;
   const int64_t grid = (int64_t)p.batch * p.h_q * p.n_pairs;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, kNW, kNB, OutT>), dim3((unsigned)grid), dim3(C::NT), 0,
-                     stream, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, kNW, kNB, kMB, OutT>), dim3((unsigned)grid), dim3(C::NT),
+                     0, stream, p);
   return hipGetLastError();
 }
 
@@ -437,15 +540,16 @@ hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
 void tile_shape_bf16(int32_t head_dim, int32_t* tq, int32_t* tk) {
   (void)head_dim;
   *tq = kNW * kNB * 32;
-  *tk = kBK;
+  *tk = kMB * 32;
 }
 
 hipError_t launch_fwd_bf16(const FwdParams& p0, int32_t head_dim, int32_t out_dtype,
                            hipStream_t stream) {
   FwdParams p = p0;
   const int bq = kNW * kNB * 32;
+  const int bk = kMB * 32;
   p.n_qtiles = (int32_t)((p.n_loc + bq - 1) / bq);
-  p.n_ktiles = (int32_t)((p.n_loc + kBK - 1) / kBK);
+  p.n_ktiles = (int32_t)((p.n_loc + bk - 1) / bk);
   p.n_pairs = (p.n_qtiles + 1) / 2;
   if (head_dim == 128)
     return out_dtype == RA_F32 ? launch_one<128, float>(p, stream) : launch_one<128, __bf16>(p, stream);
