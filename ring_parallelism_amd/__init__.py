@@ -21,7 +21,9 @@ OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 MAX_BLOCKS = 128
 MAX_PARTS = 64
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libring_attn.so")
+# RING_ATTN_LIB may name another build of the same library (tuning variants).
+LIB_PATH = os.environ.get("RING_ATTN_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                           "libring_attn.so")
 
 EXPORTS = ("zigzag_partition", "zigzag_unpartition", "ring_attn_shard_fwd", "ring_attn_tile_shape",
            "ring_attn_merge", "ring_attn_last_error", "ring_attn_abi_version")

@@ -42,6 +42,18 @@
 
 #include "ra_common.h"
 
+// Tile configuration: waves per workgroup, 32-row query blocks per wave,
+// 32-key blocks per pipeline step.  (Compile-time knobs for tuning sweeps.)
+#ifndef RA_FWD_NW
+#define RA_FWD_NW 8
+#endif
+#ifndef RA_FWD_NB
+#define RA_FWD_NB 1
+#endif
+#ifndef RA_FWD_MB
+#define RA_FWD_MB 1
+#endif
+
 namespace ra {
 namespace {
 
@@ -75,6 +87,9 @@ __device__ inline void lds_load16(__amdgpu_buffer_rsrc_t r, lds_char* dst, uint3
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
 }
 
+template <int V>
+using Ic = std::integral_constant<int, V>;
+
 template <int D, int NW, int NB, int MB>
 struct Cfg {
   static constexpr int NT = NW * 64;
@@ -84,7 +99,7 @@ struct Cfg {
   static constexpr int CHUNKS = ROWB / 16;            // 16-byte chunks per row
   static constexpr int TILEB = BK * ROWB;             // bytes per K or V tile
   static constexpr int STAGEB = 2 * TILEB;            // K tile then V tile
-  static constexpr int STAGES = 3;
+  static constexpr int STAGES = 4;
   static constexpr int RPI = 1024 / ROWB;             // rows per 64-lane 16-byte load
   static constexpr int LOADS = TILEB / 1024 / NW;     // loads per wave per tile, each tensor
   static_assert(LOADS >= 1 && TILEB % (1024 * NW) == 0, "tile must split evenly over waves");
@@ -104,15 +119,20 @@ template <int D, int NW, int NB, int MB, typename OutT>
 __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
   using C = Cfg<D, NW, NB, MB>;
   constexpr int kBK = C::BK;
-  // Three LDS stages as separate objects: the compiler then knows that the
+  // The LDS stages are separate objects: the compiler then knows that the
   // LDS-direct loads filling one stage cannot alias reads of another, and does
   // not make those reads wait for the loads in flight.
   __shared__ __attribute__((aligned(1024))) char smem0[C::STAGEB];
   __shared__ __attribute__((aligned(1024))) char smem1[C::STAGEB];
   __shared__ __attribute__((aligned(1024))) char smem2[C::STAGEB];
+  __shared__ __attribute__((aligned(1024))) char smem3[C::STAGEB];
   auto stage = [&](auto S) -> lds_char* {
     constexpr int st = decltype(S)::value;
-    return st == 0 ? (lds_char*)smem0 : (st == 1 ? (lds_char*)smem1 : (lds_char*)smem2);
+    static_assert(st < C::STAGES, "stage index");
+    if constexpr (st == 0) return (lds_char*)smem0;
+    if constexpr (st == 1) return (lds_char*)smem1;
+    if constexpr (st == 2) return (lds_char*)smem2;
+    return (lds_char*)smem3;
   };
 
   const int tid = threadIdx.x;
@@ -363,10 +383,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       }
     };
 
-    // Software pipeline over the tile sequence, three LDS stages in a ring.
-    // Step i: loads of tile i+2 in flight; the scores of tile i+1 (matrix
-    // cores) run beside the exponentials of tile i (vector unit); then the
-    // value product of tile i runs beside the max and shift of tile i+1.
+    // Software pipeline over the tile sequence, four LDS stages in a ring.
+    // Step i: loads of tile i+3 issued (tile i+2 already in flight); the
+    // scores of tile i+1 run on the matrix cores beside the exponentials of
+    // tile i on the vector unit; then the value product of tile i runs beside
+    // the max and shift of tile i+1.  One workgroup barrier per step.
     Tile t0;
     t0.t = -1;
     t0.kt = 0;
@@ -376,12 +397,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       block_counts(t0);
       if (t0.vis > 0) break;
     }
-    Tile t1 = advance(t0), t2 = advance(t1);
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    if (valid(t0)) issue_loads(stage(I0{}), t0);
-    if (valid(t1)) issue_loads(stage(I1{}), t1);
+    Tile t1 = advance(t0), t2 = advance(t1), t3 = advance(t2);
+    if (valid(t0)) issue_loads(stage(Ic<0>{}), t0);
+    if (valid(t1)) issue_loads(stage(Ic<1>{}), t1);
+    if (valid(t2)) issue_loads(stage(Ic<2>{}), t2);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
@@ -389,17 +408,17 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
     bf16x8 pb[NB][2 * MB];
     float mt[NB];
     if (valid(t0)) {
-      qk(xa, stage(I0{}));
+      qk(xa, stage(Ic<0>{}));
       if (t0.kt >= t0.full) mask(xa, t0);
       row_max(xa, mt);
       shift(xa);
       rescale(mt, xa);  // first reference max (O and l are still zero)
     }
 
-    // One pipeline step; S0, S1, S2 are the (compile-time) stages of tiles
-    // i, i+1, i+2.  Returns false once tile i+1 is past the end.
-    auto step = [&](auto S0, auto S1, auto S2, f32x16 (&x)[MB][NB], f32x16 (&y)[MB][NB]) {
-      if (valid(t2)) issue_loads(stage(S2), t2);
+    // One step; S0, S1, S3 are the (compile-time) stages of tiles i, i+1,
+    // i+3.  Returns false once the tile sequence is exhausted.
+    auto step = [&](auto S0, auto S1, auto S3, f32x16 (&x)[MB][NB], f32x16 (&y)[MB][NB]) {
+      if (valid(t3)) issue_loads(stage(S3), t3);
       qk(y, stage(S1));  // harmless when t1 is past the end: its result is unused
       exps(x, pb);
       // Materialise P here, beside the score products, rather than after the
@@ -422,23 +441,27 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
         asm volatile("" ::: "memory");
         rescale(mt, y);
       }
-      // Tile i+2 must have landed before the next step reads it, and stage
-      // S0 must be drained before the next step refills it.
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // Tile i+2 (issued a step earlier) must have landed before the next
+      // step reads it; this step's loads may stay in flight.  Stage S0 must
+      // be drained before a later step refills it.
+      if (valid(t3)) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C::LOADS) : "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
       __syncthreads();
       t0 = t1;
       t1 = t2;
-      t2 = advance(t2);
+      t2 = t3;
+      t3 = advance(t3);
       return valid(t0);
     };
-    // Stages rotate with period 3 and the score buffers with period 2.
+    // Stages rotate with period 4 and the score buffers with period 2.
     while (valid(t0)) {
-      if (!step(I0{}, I1{}, I2{}, xa, xb)) break;
-      if (!step(I1{}, I2{}, I0{}, xb, xa)) break;
-      if (!step(I2{}, I0{}, I1{}, xa, xb)) break;
-      if (!step(I0{}, I1{}, I2{}, xb, xa)) break;
-      if (!step(I1{}, I2{}, I0{}, xa, xb)) break;
-      if (!step(I2{}, I0{}, I1{}, xb, xa)) break;
+      if (!step(Ic<0>{}, Ic<1>{}, Ic<3>{}, xa, xb)) break;
+      if (!step(Ic<1>{}, Ic<2>{}, Ic<0>{}, xb, xa)) break;
+      if (!step(Ic<2>{}, Ic<3>{}, Ic<1>{}, xa, xb)) break;
+      if (!step(Ic<3>{}, Ic<0>{}, Ic<2>{}, xb, xa)) break;
     }
 
     // Epilogue: out = O / l, lse = ln 2 * (m_ref + log2 l).
@@ -512,45 +535,44 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-// Tile configuration: waves per workgroup, 32-row query blocks per wave,
-// 32-key blocks per pipeline step.  (Compile-time knobs for tuning sweeps.)
-#ifndef RA_FWD_NW
-#define RA_FWD_NW 4
-#endif
-#ifndef RA_FWD_NB
-#define RA_FWD_NB 2
-#endif
-#ifndef RA_FWD_MB
-#define RA_FWD_MB 1
-#endif
-constexpr int kNW = RA_FWD_NW, kNB = RA_FWD_NB, kMB = RA_FWD_MB;
+// Per head_dim tile configuration (waves, 32-row blocks per wave, 32-key blocks per step).
+template <int D>
+struct TileCfg {
+  static constexpr int NW = RA_FWD_NW, NB = RA_FWD_NB, MB = RA_FWD_MB;
+};
+template <>
+struct TileCfg<64> {  // the d = 64 tiles are too small to split over more than 4 waves
+  static constexpr int NW = 4, NB = 2, MB = 1;
+};
 
 template <int D, typename OutT>
-hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
-  using C = Cfg<D, kNW, kNB, kMB>;
+hipError_t launch_one(FwdParams p, hipStream_t stream) {
+  using T = TileCfg<D>;
+  using C = Cfg<D, T::NW, T::NB, T::MB>;
+  p.n_qtiles = (int32_t)((p.n_loc + C::BQ - 1) / C::BQ);
+  p.n_ktiles = (int32_t)((p.n_loc + C::BK - 1) / C::BK);
+  p.n_pairs = (p.n_qtiles + 1) / 2;
   const int64_t grid = (int64_t)p.batch * p.h_q * p.n_pairs;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, kNW, kNB, kMB, OutT>), dim3((unsigned)grid), dim3(C::NT),
-                     0, stream, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, T::NW, T::NB, T::MB, OutT>), dim3((unsigned)grid),
+                     dim3(C::NT), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 void tile_shape_bf16(int32_t head_dim, int32_t* tq, int32_t* tk) {
-  (void)head_dim;
-  *tq = kNW * kNB * 32;
-  *tk = kMB * 32;
+  if (head_dim == 64) {
+    *tq = TileCfg<64>::NW * TileCfg<64>::NB * 32;
+    *tk = TileCfg<64>::MB * 32;
+  } else {
+    *tq = TileCfg<128>::NW * TileCfg<128>::NB * 32;
+    *tk = TileCfg<128>::MB * 32;
+  }
 }
 
-hipError_t launch_fwd_bf16(const FwdParams& p0, int32_t head_dim, int32_t out_dtype,
+hipError_t launch_fwd_bf16(const FwdParams& p, int32_t head_dim, int32_t out_dtype,
                            hipStream_t stream) {
-  FwdParams p = p0;
-  const int bq = kNW * kNB * 32;
-  const int bk = kMB * 32;
-  p.n_qtiles = (int32_t)((p.n_loc + bq - 1) / bq);
-  p.n_ktiles = (int32_t)((p.n_loc + bk - 1) / bk);
-  p.n_pairs = (p.n_qtiles + 1) / 2;
   if (head_dim == 128)
     return out_dtype == RA_F32 ? launch_one<128, float>(p, stream) : launch_one<128, __bf16>(p, stream);
   return out_dtype == RA_F32 ? launch_one<64, float>(p, stream) : launch_one<64, __bf16>(p, stream);
