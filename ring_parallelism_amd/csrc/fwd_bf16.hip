@@ -53,6 +53,12 @@
 #ifndef RA_FWD_MB
 #define RA_FWD_MB 1
 #endif
+#ifndef RA_FWD_STAGES
+#define RA_FWD_STAGES 6
+#endif
+#ifndef RA_FWD_PAIRED
+#define RA_FWD_PAIRED 1
+#endif
 
 namespace ra {
 namespace {
@@ -90,6 +96,17 @@ __device__ inline void lds_load16(__amdgpu_buffer_rsrc_t r, lds_char* dst, uint3
 template <int V>
 using Ic = std::integral_constant<int, V>;
 
+// Calls f(Ic<I>), f(Ic<I+1>), ..., f(Ic<N-1>) while each call returns true.
+template <int I, int N, typename F>
+__device__ inline bool unrolled_steps(F& f) {
+  if constexpr (I == N) {
+    return true;
+  } else {
+    if (!f(Ic<I>{})) return false;
+    return unrolled_steps<I + 1, N>(f);
+  }
+}
+
 template <int D, int NW, int NB, int MB>
 struct Cfg {
   static constexpr int NT = NW * 64;
@@ -99,7 +116,11 @@ struct Cfg {
   static constexpr int CHUNKS = ROWB / 16;            // 16-byte chunks per row
   static constexpr int TILEB = BK * ROWB;             // bytes per K or V tile
   static constexpr int STAGEB = 2 * TILEB;            // K tile then V tile
-  static constexpr int STAGES = 4;
+  static constexpr int STAGES = RA_FWD_STAGES;  // LDS ring depth (4..6)
+  static_assert(STAGES >= 4 && STAGES <= 6, "stages");
+  // One barrier per two steps (loads issued two tiles at a time); needs 6 stages.
+  static constexpr bool PAIRED = RA_FWD_PAIRED != 0;
+  static_assert(!PAIRED || STAGES == 6, "paired steps use six stages");
   static constexpr int RPI = 1024 / ROWB;             // rows per 64-lane 16-byte load
   static constexpr int LOADS = TILEB / 1024 / NW;     // loads per wave per tile, each tensor
   static_assert(LOADS >= 1 && TILEB % (1024 * NW) == 0, "tile must split evenly over waves");
@@ -126,13 +147,17 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) char smem1[C::STAGEB];
   __shared__ __attribute__((aligned(1024))) char smem2[C::STAGEB];
   __shared__ __attribute__((aligned(1024))) char smem3[C::STAGEB];
+  __shared__ __attribute__((aligned(1024))) char smem4[C::STAGES > 4 ? C::STAGEB : 16];
+  __shared__ __attribute__((aligned(1024))) char smem5[C::STAGES > 5 ? C::STAGEB : 16];
   auto stage = [&](auto S) -> lds_char* {
     constexpr int st = decltype(S)::value;
     static_assert(st < C::STAGES, "stage index");
     if constexpr (st == 0) return (lds_char*)smem0;
     if constexpr (st == 1) return (lds_char*)smem1;
     if constexpr (st == 2) return (lds_char*)smem2;
-    return (lds_char*)smem3;
+    if constexpr (st == 3) return (lds_char*)smem3;
+    if constexpr (st == 4) return (lds_char*)smem4;
+    return (lds_char*)smem5;
   };
 
   const int tid = threadIdx.x;
@@ -383,43 +408,78 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       }
     };
 
-    // Software pipeline over the tile sequence, four LDS stages in a ring.
-    // Step i: loads of tile i+3 issued (tile i+2 already in flight); the
-    // scores of tile i+1 run on the matrix cores beside the exponentials of
-    // tile i on the vector unit; then the value product of tile i runs beside
-    // the max and shift of tile i+1.  One workgroup barrier per step.
-    Tile t0;
-    t0.t = -1;
-    t0.kt = 0;
-    t0.vis = 0;
-    t0.full = 0;
-    while (++t0.t < p.n_blocks) {
-      block_counts(t0);
-      if (t0.vis > 0) break;
+    // Software pipeline over the tile sequence, C::STAGES LDS stages in a
+    // ring.  Step i: loads of tile i+STAGES-1 issued (tiles i+2.. already in
+    // flight); the scores of tile i+1 run on the matrix cores beside the
+    // exponentials of tile i on the vector unit; then the value product of
+    // tile i runs beside the max and shift of tile i+1.  One workgroup
+    // barrier per step.  Two cursors walk the tile list: `ld` (the tile being
+    // loaded) and `nx` (tile i+1); n_tiles bounds both.
+    constexpr int NS = C::STAGES;
+    Tile first;
+    first.t = -1;
+    first.kt = 0;
+    first.vis = 0;
+    first.full = 0;
+    int n_tiles = 0;
+    for (int t = 0; t < p.n_blocks; ++t) {
+      Tile x;
+      x.t = t;
+      block_counts(x);
+      if (x.vis > 0 && first.t < 0) first = x;
+      n_tiles += x.vis;
     }
-    Tile t1 = advance(t0), t2 = advance(t1), t3 = advance(t2);
-    if (valid(t0)) issue_loads(stage(Ic<0>{}), t0);
-    if (valid(t1)) issue_loads(stage(Ic<1>{}), t1);
-    if (valid(t2)) issue_loads(stage(Ic<2>{}), t2);
+    Tile ld = first, nx = first;
+    if (n_tiles > 0) issue_loads(stage(Ic<0>{}), ld);
+    ld = advance(ld);
+    nx = ld;
+    if (n_tiles > 1) issue_loads(stage(Ic<1>{}), ld);
+    ld = advance(ld);
+    if (n_tiles > 2) issue_loads(stage(Ic<2>{}), ld);
+    ld = advance(ld);
+    if constexpr (NS > 4) {
+      if (n_tiles > 3) issue_loads(stage(Ic<3>{}), ld);
+      ld = advance(ld);
+    }
+    if constexpr (NS > 5 && !C::PAIRED) {
+      if (n_tiles > 4) issue_loads(stage(Ic<4>{}), ld);
+      ld = advance(ld);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
     f32x16 xa[MB][NB], xb[MB][NB];
     bf16x8 pb[NB][2 * MB];
     float mt[NB];
-    if (valid(t0)) {
+    if (n_tiles > 0) {
       qk(xa, stage(Ic<0>{}));
-      if (t0.kt >= t0.full) mask(xa, t0);
+      if (first.kt >= first.full) mask(xa, first);
       row_max(xa, mt);
       shift(xa);
       rescale(mt, xa);  // first reference max (O and l are still zero)
     }
 
-    // One step; S0, S1, S3 are the (compile-time) stages of tiles i, i+1,
-    // i+3.  Returns false once the tile sequence is exhausted.
-    auto step = [&](auto S0, auto S1, auto S3, f32x16 (&x)[MB][NB], f32x16 (&y)[MB][NB]) {
-      if (valid(t3)) issue_loads(stage(S3), t3);
-      qk(y, stage(S1));  // harmless when t1 is past the end: its result is unused
+    // Step i at compile-time rotation position K: tiles i, i+1 and i+NS-1
+    // live in stages K, K+1 and K+NS-1 (mod NS); the score buffers swap each
+    // step.  Returns false once tile i+1 is past the end.
+    int i = 0;
+    auto step = [&](auto K) {
+      constexpr int k = decltype(K)::value;
+      auto& x = (k % 2 == 0) ? xa : xb;
+      auto& y = (k % 2 == 0) ? xb : xa;
+      const bool has_next = i + 1 < n_tiles;
+      if constexpr (!C::PAIRED) {
+        if (i + NS - 1 < n_tiles) issue_loads(stage(Ic<(k + NS - 1) % NS>{}), ld);
+        ld = advance(ld);
+      } else if constexpr (k % 2 == 0) {
+        // Paired steps: tiles i+4 and i+5 refill the stages of tiles i-2 and
+        // i-1, released by the barrier that closed step i-1.
+        if (i + 4 < n_tiles) issue_loads(stage(Ic<(k + 4) % NS>{}), ld);
+        ld = advance(ld);
+        if (i + 5 < n_tiles) issue_loads(stage(Ic<(k + 5) % NS>{}), ld);
+        ld = advance(ld);
+      }
+      qk(y, stage(Ic<(k + 1) % NS>{}));  // harmless when there is no tile i+1
       exps(x, pb);
       // Materialise P here, beside the score products, rather than after the
       // (rare) mask branch below.
@@ -427,13 +487,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int k4 = 0; k4 < 2 * MB; ++k4) asm volatile("" : "+v"(pb[nb][k4]));
-      if (valid(t1) && t1.kt >= t1.full) mask(y, t1);
-      pv(stage(S0), pb);
+      if (has_next && nx.kt >= nx.full) mask(y, nx);
+      pv(stage(Ic<k % NS>{}), pb);
       row_max(y, mt);
       bool need = false;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) need |= mt[nb] > m_ref[nb] + kRescaleThreshold;
-      need = need && valid(t1);
+      need = need && has_next;
       shift(y);
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
         // Rare path: keep it a real branch (if-converting it would put the
@@ -441,27 +501,33 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
         asm volatile("" ::: "memory");
         rescale(mt, y);
       }
-      // Tile i+2 (issued a step earlier) must have landed before the next
-      // step reads it; this step's loads may stay in flight.  Stage S0 must
-      // be drained before a later step refills it.
-      if (valid(t3)) {
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C::LOADS) : "memory");
-      } else {
+      if constexpr (!C::PAIRED) {
+        // Tile i+2 must have landed before the next step reads it; the loads
+        // of tiles i+3 .. i+NS-1 may stay in flight.  Stage K must be drained
+        // before a later step refills it.
+        if (i + NS - 1 < n_tiles) {
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 3) * 2 * C::LOADS) : "memory");
+        } else {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        __syncthreads();
+      } else if constexpr (k % 2 == 1) {
+        // The tiles loaded at step i-1 are read from step i+2 on.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
       }
-      __syncthreads();
-      t0 = t1;
-      t1 = t2;
-      t2 = t3;
-      t3 = advance(t3);
-      return valid(t0);
+      nx = advance(nx);
+      return ++i < n_tiles;
     };
-    // Stages rotate with period 4 and the score buffers with period 2.
-    while (valid(t0)) {
-      if (!step(Ic<0>{}, Ic<1>{}, Ic<3>{}, xa, xb)) break;
-      if (!step(Ic<1>{}, Ic<2>{}, Ic<0>{}, xb, xa)) break;
-      if (!step(Ic<2>{}, Ic<3>{}, Ic<1>{}, xa, xb)) break;
-      if (!step(Ic<3>{}, Ic<0>{}, Ic<2>{}, xb, xa)) break;
+    // Stages rotate with period NS and the score buffers with period 2.
+    constexpr int kUnroll = NS % 2 == 0 ? NS : 2 * NS;
+    while (i < n_tiles) {
+      if (!unrolled_steps<0, kUnroll>(step)) break;
+    }
+    if constexpr (C::PAIRED) {
+      // A final barrier: the sequence may end between the paired barriers.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
     }
 
     // Epilogue: out = O / l, lse = ln 2 * (m_ref + log2 l).
