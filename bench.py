@@ -69,6 +69,22 @@ def cpu_baseline(w, target_s):
                       f"({flop / 1e9:.1f} GFLOP useful in {elapsed:.1f} s, fp64, timed around the oracle call)"}
 
 
+def measured_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when the kernel source has changed since the counters were taken."""
+    import hashlib
+    prof = os.path.join(ROOT, "profiles", "fwd_bf16_s128k_c16_zigzag_hbm_traffic.md")
+    src = os.path.join(ROOT, "ring_parallelism_amd", "csrc", "fwd_bf16.hip")
+    try:
+        fields = dict(line.split(": ", 1) for line in open(prof).read().splitlines() if ": " in line)
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if fields.get("source_sha256", "").strip() != sha:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,7 +182,8 @@ def main():
                    "shards_per_step": c, "inputs": f"N(0,{w.sigma}^2) seeded, bf16-rounded" if w.dtype == "bf16" else "N(0,1) seeded"},
         "pct_of_peak": round(100.0 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": round(peak, 1),
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic() if w.name == "s128k_c16_zigzag_16x1" else None,
                      "kernel": "fwd_bf16_kernel" if w.dtype == "bf16" else "fwd_f32_kernel",
                      "flop_per_launch": flop_launch, "avg_launch_ms": round(avg_kernel_s * 1e3, 4),
                      "launches_timed": len(kernel_ms)},
