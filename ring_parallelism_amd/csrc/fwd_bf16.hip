@@ -26,10 +26,14 @@
 // the ds_read_b128 of K and the transposing reads of V hit distinct banks.
 //
 // The softmax works in the log2 domain (scale * log2 e folded into one fma
-// before v_exp_f32).  The reference max only moves when a tile's max exceeds
-// it by more than 8 (log2 units), so exp2 arguments stay <= 8 and the output
-// rescale runs on a few tiles per row instead of every tile; l and O share
-// the reference, so the result is the same up to rounding.
+// before v_exp_f32) against a per-row reference m that is a real score max
+// but may trail the running max: any reference works as long as O and l
+// share it, so the result is the same up to rounding.  No per-tile row max is
+// taken.  The exponentials of a tile are summed anyway (for l); when a lane's
+// 16-term sum exceeds 2^16 -- some exponent above 16 -- the tile is redone
+// after raising m to its true max and rescaling O and l.  Exponents therefore
+// stay <= 16 (nothing can overflow), and the max, rescale and redo run on a
+// handful of tiles per row.
 //
 // Workgroup: NW wavefronts x NB 32-row blocks = BQ query rows of one
 // (batch, head).  Each workgroup takes query tiles p and n_qtiles-1-p of the
@@ -68,7 +72,9 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr float kRescaleThreshold = 8.0f;
+// Largest 16-term in-lane sum of exponentials accepted without raising the
+// reference (each term is then <= 2^16).
+constexpr float kSumLimit = 65536.0f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
 
@@ -230,11 +236,18 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
 
     // Tile iterator over (block t, key tile kt), skipping blocks with no
     // visible key.  A state is (t, kt, n_vis, n_full); t >= n_blocks: done.
+    // The cursor also carries the block's K and V base addresses, read from
+    // the argument block once per block: a scalar load in the per-tile path
+    // would make every tile wait for all of the wave's LDS reads as well.
     struct Tile {
       int t, kt, vis, full;
+      const __bf16* kb;
+      const __bf16* vb;
     };
     auto block_counts = [&](Tile& x) {
       const int j = p.owner[x.t];
+      x.kb = (const __bf16*)p.k[x.t] + kv_off;
+      x.vb = (const __bf16*)p.v[x.t] + kv_off;
       const int c_last = p.causal ? count_upto32(j, pos_last, n_loc, p.c, p.split) : n_loc;
       const int c_first = p.causal ? count_upto32(j, pos_first, n_loc, p.c, p.split) : n_loc;
       x.vis = (c_last + kBK - 1) / kBK;
@@ -255,10 +268,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
     // Put tile x's K and V into LDS stage `st`.  Rows past the shard end fall
     // outside the buffer resource and read as zeros.
     auto issue_loads = [&](lds_char* kdst, const Tile& x) {
-      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)((const __bf16*)p.k[x.t] + kv_off), (short)0, kv_bytes, kRsrcWord3);
-      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)((const __bf16*)p.v[x.t] + kv_off), (short)0, kv_bytes, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc((void*)x.kb, (short)0, kv_bytes, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc((void*)x.vb, (short)0, kv_bytes, kRsrcWord3);
       lds_char* vdst = kdst + C::TILEB;
 #pragma unroll
       for (int u = 0; u < C::LOADS; ++u) {
@@ -330,6 +343,20 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       }
     };
 
+    // Tile max in absolute log2 units of x values already shifted by the
+    // reference (x = scale*log2(e)*s - m_ref; m_ref = -inf: shifted by 0).
+    auto xmax = [&](const f32x16 (&x)[MB][NB], float (&mt)[NB]) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x[mb][nb][i]);
+        mt[nb] = halves_max(mx) + ((m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb]);
+      }
+    };
+
     // x = scale*log2(e)*s - m_ref, in place (m_ref = -inf: shift by 0).
     auto shift = [&](f32x16 (&sacc)[MB][NB]) {
 #pragma unroll
@@ -342,8 +369,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       }
     };
 
-    // Raise the reference max where a tile's max exceeds it by more than the
-    // threshold: rescale O and l, and re-shift the pending tile's x values.
+    // Raise the reference to the tile max mt (absolute, log2 units) where it
+    // is higher: rescale O and l, and re-shift the tile's x values.
     auto rescale = [&](const float (&mt)[NB], f32x16 (&xnext)[MB][NB]) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -363,12 +390,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       }
     };
 
-    // P = bf16(exp2(x)) as the B operand of the value product; l gathers
-    // the fp32 sum (the log-sum-exp needs it unrounded).
-    auto exps = [&](const f32x16 (&x)[MB][NB], bf16x8 (&pb)[NB][2 * MB]) {
+    // P = bf16(exp2(x)) as the B operand of the value product; ls gets the
+    // lane's fp32 sum of the tile (the log-sum-exp needs it unrounded).
+    auto exps = [&](const f32x16 (&x)[MB][NB], bf16x8 (&pb)[NB][2 * MB], float (&ls)[NB]) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        float ls = 0.f;
+        float sum = 0.f;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -377,42 +404,71 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const float pe = __builtin_amdgcn_exp2f(x[mb][nb][hh * 8 + e]);
-              ls += pe;
+              sum = (mb == 0 && hh == 0 && e == 0) ? pe : sum + pe;
               v8[e] = (__bf16)pe;
             }
             pb[nb][mb * 2 + hh] = v8;
           }
-        l_part[nb] += ls;
+        ls[nb] = sum;
       }
     };
 
-    // O^T += V^T P^T for the tile in stage st, 16 keys per MFMA step.
+    // Rows whose reference is still unset (no visible key folded yet) take
+    // the max-based path on every tile until they get one.
+    auto any_unset = [&]() {
+      bool u = false;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) u |= m_ref[nb] == -INFINITY && posq[nb] >= 0;
+      return __builtin_amdgcn_ballot_w64(u) != 0;
+    };
+
+    // O^T += V^T P^T for the tile in stage st, 16 keys per MFMA step.  The
+    // transposing reads are issued as inline assembly: the compiler cannot
+    // tell that they miss the stages the LDS-direct loads are filling, and
+    // would otherwise wait for every load in flight before the first one.
+    // Their completion is awaited explicitly (lgkmcnt counts LDS reads in
+    // issue order, and nothing else touches LDS between these statements).
     auto pv = [&](const lds_char* stage_base, const bf16x8 (&pb)[NB][2 * MB]) {
       const lds_char* vs = stage_base + C::TILEB;
+      constexpr int ND = D / 32, NK = 2 * MB;
+      bf16x8 a[2][NK];
+      auto reads = [&](int db, bf16x8 (&dst)[NK]) {
+        const int row = v_row;
+        const int d = db * 32 + v_d;
+        const uint32_t addr = (uint32_t)(uintptr_t)(vs + row * C::ROWB + C::v_slot(row, d >> 3) * 16 + (d & 7) * 2);
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
+        for (int k16 = 0; k16 < NK; ++k16) {
+          bf16x4 lo, hi;
+          asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(addr), "n"(k16 * 16 * C::ROWB));
+          asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(addr), "n"((k16 * 16 + 8) * C::ROWB));
+          dst[k16] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      };
+      reads(0, a[0]);
 #pragma unroll
-        for (int k16 = 0; k16 < 2 * MB; ++k16) {
-          const int row = k16 * 16 + v_row;
-          const int d = db * 32 + v_d;
-          const int off = row * C::ROWB + C::v_slot(row, d >> 3) * 16 + (d & 7) * 2;
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4*)(vs + off));
-          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4*)(vs + off + 8 * C::ROWB));
-          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      for (int db = 0; db < ND; ++db) {
+        auto& cur = a[db & 1];
+        static_assert(NK == 2, "one 32-key block per step");
+        if (db + 1 < ND) {
+          reads(db + 1, a[(db + 1) & 1]);
+          asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(cur[0]), "+v"(cur[1]) : "n"(2 * NK));
+        } else {
+          asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(cur[0]), "+v"(cur[1]));
+        }
+#pragma unroll
+        for (int k16 = 0; k16 < NK; ++k16)
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
-            oacc[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[nb][k16], oacc[db][nb], 0, 0, 0);
-        }
+            oacc[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[k16], pb[nb][k16], oacc[db][nb], 0, 0, 0);
       }
     };
 
     // Software pipeline over the tile sequence, C::STAGES LDS stages in a
-    // ring.  Step i: loads of tile i+STAGES-1 issued (tiles i+2.. already in
-    // flight); the scores of tile i+1 run on the matrix cores beside the
-    // exponentials of tile i on the vector unit; then the value product of
-    // tile i runs beside the max and shift of tile i+1.  One workgroup
+    // ring.  Step i: the scores of tile i+1 run on the matrix cores beside
+    // the exponentials of tile i on the vector unit; then the value product
+    // of tile i runs beside the shift of tile i+1.  Loads run STAGES-2 tiles
+    // ahead: with paired steps, every even step issues two tiles and every
+    // odd step ends with the workgroup barrier; otherwise one tile and one
     // barrier per step.  Two cursors walk the tile list: `ld` (the tile being
     // loaded) and `nx` (tile i+1); n_tiles bounds both.
     constexpr int NS = C::STAGES;
@@ -421,6 +477,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
     first.kt = 0;
     first.vis = 0;
     first.full = 0;
+    first.kb = first.vb = nullptr;
     int n_tiles = 0;
     for (int t = 0; t < p.n_blocks; ++t) {
       Tile x;
@@ -450,13 +507,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
 
     f32x16 xa[MB][NB], xb[MB][NB];
     bf16x8 pb[NB][2 * MB];
-    float mt[NB];
+    float mt[NB], ls[NB];
+    bool unset = false;
     if (n_tiles > 0) {
       qk(xa, stage(Ic<0>{}));
       if (first.kt >= first.full) mask(xa, first);
       row_max(xa, mt);
       shift(xa);
       rescale(mt, xa);  // first reference max (O and l are still zero)
+      unset = any_unset();
     }
 
     // Step i at compile-time rotation position K: tiles i, i+1 and i+NS-1
@@ -480,27 +539,36 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
         ld = advance(ld);
       }
       qk(y, stage(Ic<(k + 1) % NS>{}));  // harmless when there is no tile i+1
-      exps(x, pb);
-      // Materialise P here, beside the score products, rather than after the
-      // (rare) mask branch below.
+      exps(x, pb, ls);
+      bool over = false;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) over |= ls[nb] > kSumLimit;
+      if ((__builtin_amdgcn_ballot_w64(over) != 0) | unset) {
+        // Rare path (a real branch: if-converting it would put the output
+        // rescale on every tile): raise the reference to tile i's max and
+        // redo its exponentials.
+        asm volatile("" ::: "memory");
+        xmax(x, mt);
+        rescale(mt, x);
+        exps(x, pb, ls);
+        unset = any_unset();
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) l_part[nb] += ls[nb];
+      // Materialise P here, beside the score products.
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int k4 = 0; k4 < 2 * MB; ++k4) asm volatile("" : "+v"(pb[nb][k4]));
       if (has_next && nx.kt >= nx.full) mask(y, nx);
       pv(stage(Ic<k % NS>{}), pb);
-      row_max(y, mt);
-      bool need = false;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) need |= mt[nb] > m_ref[nb] + kRescaleThreshold;
-      need = need && has_next;
       shift(y);
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {
-        // Rare path: keep it a real branch (if-converting it would put the
-        // whole output rescale on every tile).
-        asm volatile("" ::: "memory");
-        rescale(mt, y);
-      }
+      // Keep the shift beside the value product (left alone, it sinks into
+      // the next step, where the vector unit already has the exponentials).
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+v"(y[mb][nb]));
       if constexpr (!C::PAIRED) {
         // Tile i+2 must have landed before the next step reads it; the loads
         // of tiles i+3 .. i+NS-1 may stay in flight.  Stage K must be drained
