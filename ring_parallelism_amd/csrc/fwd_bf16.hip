@@ -92,11 +92,12 @@ __device__ inline float halves_sum(float x) {
 }
 
 // 16 bytes per lane from a buffer resource straight into LDS: lane i's data
-// lands at dst + 16 * i (dst is wave-uniform); out-of-range offsets read 0.
+// lands at dst + 16 * i (dst is wave-uniform); the byte offset is the lane's
+// voff plus the wave-uniform soff, and out-of-range offsets read 0.
 // Kept as a plain device function: the host pass of a kernel template that
 // names this builtin directly emits no launch stub.
-__device__ inline void lds_load16(__amdgpu_buffer_rsrc_t r, lds_char* dst, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+__device__ inline void lds_load16(__amdgpu_buffer_rsrc_t r, lds_char* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
 }
 
 template <int V>
@@ -113,6 +114,15 @@ __device__ inline bool unrolled_steps(F& f) {
   }
 }
 
+// Calls f(Ic<I>), ..., f(Ic<N-1>).
+template <int I, int N, typename F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(Ic<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 template <int D, int NW, int NB, int MB>
 struct Cfg {
   static constexpr int NT = NW * 64;
@@ -121,7 +131,6 @@ struct Cfg {
   static constexpr int ROWB = D * 2;                  // bytes per K / V row
   static constexpr int CHUNKS = ROWB / 16;            // 16-byte chunks per row
   static constexpr int TILEB = BK * ROWB;             // bytes per K or V tile
-  static constexpr int STAGEB = 2 * TILEB;            // K tile then V tile
   static constexpr int STAGES = RA_FWD_STAGES;  // LDS ring depth (4..6)
   static_assert(STAGES >= 4 && STAGES <= 6, "stages");
   // One barrier per two steps (loads issued two tiles at a time); needs 6 stages.
@@ -146,25 +155,17 @@ template <int D, int NW, int NB, int MB, typename OutT>
 __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
   using C = Cfg<D, NW, NB, MB>;
   constexpr int kBK = C::BK;
-  // The LDS stages are separate objects: the compiler then knows that the
-  // LDS-direct loads filling one stage cannot alias reads of another, and does
-  // not make those reads wait for the loads in flight.
-  __shared__ __attribute__((aligned(1024))) char smem0[C::STAGEB];
-  __shared__ __attribute__((aligned(1024))) char smem1[C::STAGEB];
-  __shared__ __attribute__((aligned(1024))) char smem2[C::STAGEB];
-  __shared__ __attribute__((aligned(1024))) char smem3[C::STAGEB];
-  __shared__ __attribute__((aligned(1024))) char smem4[C::STAGES > 4 ? C::STAGEB : 16];
-  __shared__ __attribute__((aligned(1024))) char smem5[C::STAGES > 5 ? C::STAGEB : 16];
-  auto stage = [&](auto S) -> lds_char* {
-    constexpr int st = decltype(S)::value;
-    static_assert(st < C::STAGES, "stage index");
-    if constexpr (st == 0) return (lds_char*)smem0;
-    if constexpr (st == 1) return (lds_char*)smem1;
-    if constexpr (st == 2) return (lds_char*)smem2;
-    if constexpr (st == 3) return (lds_char*)smem3;
-    if constexpr (st == 4) return (lds_char*)smem4;
-    return (lds_char*)smem5;
+  // One LDS array: the K tiles of the STAGES ring stages, then their V tiles.
+  // Every LDS read of the tile loop is inline assembly with the stage offset
+  // as the instruction's immediate, so per-lane addresses are computed once.
+  // (The compiler cannot tell which stage an LDS-direct load fills, and would
+  // make compiler-visible reads wait for all loads in flight.)
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGES * C::TILEB];
+  auto k_tile = [&](auto S) -> lds_char* { return (lds_char*)smem + decltype(S)::value * C::TILEB; };
+  auto v_tile = [&](auto S) -> lds_char* {
+    return (lds_char*)smem + (C::STAGES + decltype(S)::value) * C::TILEB;
   };
+  static_assert(C::STAGES * C::TILEB <= 65536, "stage offsets must fit the 16-bit LDS immediate");
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -190,11 +191,33 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
   // LDS-direct load roles: lane -> (row in its 1 KiB group, 16-byte slot).
   const int ld_row = lane / C::CHUNKS;
   const int ld_slot = lane % C::CHUNKS;
+  // Byte offsets inside a tile (a whole number of 32-row groups: the
+  // swizzles only look at the low row bits).
+  uint32_t ld_koff[C::LOADS], ld_voff[C::LOADS];
+#pragma unroll
+  for (int u = 0; u < C::LOADS; ++u) {
+    const int row = (wave * C::LOADS + u) * C::RPI + ld_row;
+    ld_koff[u] = row * C::ROWB + C::k_slot(row, ld_slot) * 16;
+    ld_voff[u] = row * C::ROWB + C::v_slot(row, ld_slot) * 16;
+  }
 
   // Transposing-read roles for V: 16-lane group qg, lane jj inside it.
   const int qg = lane >> 4, jj = lane & 15;
   const int v_row = 4 * g + (jj >> 2);           // + 16 * step (+ 8 for the high half)
   const int v_d = 16 * (qg & 1) + 4 * (jj & 3);  // + 32 * d-block
+
+  // LDS addresses of this lane's reads in stage 0 (other stages: + immediate).
+  static_assert(MB == 1, "one 32-key block per step");
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
+  uint32_t kaddr[D / 16];  // K: key row lc, 16-byte chunk 2s+g
+#pragma unroll
+  for (int s16 = 0; s16 < D / 16; ++s16) kaddr[s16] = lds0 + lc * C::ROWB + C::k_slot(lc, 2 * s16 + g) * 16;
+  uint32_t vaddr[D / 32];  // V: rows v_row (+8, +16, +24), columns v_d of d-slice db
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int d = db * 32 + v_d;
+    vaddr[db] = lds0 + C::STAGES * C::TILEB + v_row * C::ROWB + C::v_slot(v_row, d >> 3) * 16 + (d & 7) * 2;
+  }
 
   uint32_t pairs_partial = 0;  // per lane, masked tiles only
 
@@ -267,40 +290,44 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
 
     // Put tile x's K and V into LDS stage `st`.  Rows past the shard end fall
     // outside the buffer resource and read as zeros.
-    auto issue_loads = [&](lds_char* kdst, const Tile& x) {
+    auto issue_loads = [&](auto S, const Tile& x) {
       const __amdgpu_buffer_rsrc_t rk =
           __builtin_amdgcn_make_buffer_rsrc((void*)x.kb, (short)0, kv_bytes, kRsrcWord3);
       const __amdgpu_buffer_rsrc_t rv =
           __builtin_amdgcn_make_buffer_rsrc((void*)x.vb, (short)0, kv_bytes, kRsrcWord3);
-      lds_char* vdst = kdst + C::TILEB;
+      const uint32_t tile_off = (uint32_t)(x.kt * kBK) * C::ROWB;
 #pragma unroll
       for (int u = 0; u < C::LOADS; ++u) {
         const int grp = wave * C::LOADS + u;  // 1 KiB group of the tile
-        const int row = grp * C::RPI + ld_row;
-        const uint32_t rowoff = (uint32_t)(x.kt * kBK + row) * C::ROWB;
-        lds_load16(rk, kdst + grp * 1024, rowoff + C::k_slot(row, ld_slot) * 16);
-        lds_load16(rv, vdst + grp * 1024, rowoff + C::v_slot(row, ld_slot) * 16);
+        lds_load16(rk, k_tile(S) + grp * 1024, ld_koff[u], tile_off);
+        lds_load16(rv, v_tile(S) + grp * 1024, ld_voff[u], tile_off);
       }
     };
 
-    // S^T = K Q^T for the tile in stage st (two 32-key blocks).
-    auto qk = [&](f32x16 (&sacc)[MB][NB], const lds_char* ks) {
+    // S^T = K Q^T for the tile in stage S: eight 16-wide slices of d, four
+    // K reads in flight ahead of the products (lgkmcnt counts LDS reads in
+    // issue order; the wait before slice s allows the reads issued after it).
+    auto qk = [&](f32x16 (&sacc)[MB][NB], auto S) {
+      constexpr int OFF = decltype(S)::value * C::TILEB;
+      constexpr int NR = D / 16, PF = 4;
+      bf16x8 a[NR];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int nb = 0; nb < NB; ++nb) sacc[0][nb] = f32x16{};
+      // (Explicit captures: clang does not capture variables that a generic
+      // lambda uses only as inline-assembly operands.)
+      static_for<0, PF>([&a, &kaddr](auto I) {
+        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(a[I]) : "v"(kaddr[I]), "n"(OFF));
+      });
+      static_for<0, NR>([&a, &kaddr, &sacc, &qreg](auto I) {
+        constexpr int sl = decltype(I)::value;
+        if constexpr (sl + PF < NR)
+          asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(a[sl + PF]) : "v"(kaddr[sl + PF]), "n"(OFF));
+        constexpr int issued = sl + PF < NR ? sl + PF + 1 : NR;
+        asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a[sl]) : "n"(issued - sl - 1));
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) sacc[mb][nb] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int row = mb * 32 + lc;
-          const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(
-              ks + row * C::ROWB + C::k_slot(row, 2 * s + g) * 16);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            sacc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[nb][s], sacc[mb][nb], 0, 0, 0);
-        }
-      }
+        for (int nb = 0; nb < NB; ++nb)
+          sacc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[sl], qreg[nb][sl], sacc[0][nb], 0, 0, 0);
+      });
     };
 
     // Elementwise mask on a tile that straddles the diagonal or the shard
@@ -422,45 +449,38 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       return __builtin_amdgcn_ballot_w64(u) != 0;
     };
 
-    // O^T += V^T P^T for the tile in stage st, 16 keys per MFMA step.  The
-    // transposing reads are issued as inline assembly: the compiler cannot
-    // tell that they miss the stages the LDS-direct loads are filling, and
-    // would otherwise wait for every load in flight before the first one.
-    // Their completion is awaited explicitly (lgkmcnt counts LDS reads in
-    // issue order, and nothing else touches LDS between these statements).
-    auto pv = [&](const lds_char* stage_base, const bf16x8 (&pb)[NB][2 * MB]) {
-      const lds_char* vs = stage_base + C::TILEB;
-      constexpr int ND = D / 32, NK = 2 * MB;
-      bf16x8 a[2][NK];
-      auto reads = [&](int db, bf16x8 (&dst)[NK]) {
-        const int row = v_row;
-        const int d = db * 32 + v_d;
-        const uint32_t addr = (uint32_t)(uintptr_t)(vs + row * C::ROWB + C::v_slot(row, d >> 3) * 16 + (d & 7) * 2);
-#pragma unroll
-        for (int k16 = 0; k16 < NK; ++k16) {
+    // The transposing reads of the V tile in stage S (for each 32-wide slice
+    // of d, two 16-key halves of 8 rows each), issued a block of work ahead
+    // of the value product so that their latency is hidden.
+    auto v_reads = [&vaddr](auto S, bf16x8 (&va)[D / 32][2 * MB]) {
+      constexpr int OFF = decltype(S)::value * C::TILEB;
+      static_for<0, D / 32>([&vaddr, &va](auto DB) {
+        static_for<0, 2 * MB>([&vaddr, &va](auto K16) {
+          constexpr int db = decltype(DB)::value, k16 = decltype(K16)::value;
+          constexpr int o = OFF + k16 * 16 * C::ROWB;
           bf16x4 lo, hi;
-          asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(addr), "n"(k16 * 16 * C::ROWB));
-          asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(addr), "n"((k16 * 16 + 8) * C::ROWB));
-          dst[k16] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-      };
-      reads(0, a[0]);
+          asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(vaddr[db]), "n"(o));
+          asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(vaddr[db]), "n"(o + 8 * C::ROWB));
+          va[db][k16] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        });
+      });
+    };
+
+    // O^T += V^T P^T, 16 keys per MFMA step, from the reads above (no other
+    // LDS read is issued in between: the wait before slice db lets the
+    // reads of the later slices stay in flight).
+    auto pv = [&](bf16x8 (&va)[D / 32][2 * MB], const bf16x8 (&pb)[NB][2 * MB]) {
+      static_assert(MB == 1, "one 32-key block per step");
+      static_for<0, D / 32>([&va, &pb, this_oacc = &oacc](auto DB) {
+        auto& oacc = *this_oacc;
+        constexpr int db = decltype(DB)::value;
+        asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(va[db][0]), "+v"(va[db][1]) : "n"(4 * (D / 32 - 1 - db)));
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        auto& cur = a[db & 1];
-        static_assert(NK == 2, "one 32-key block per step");
-        if (db + 1 < ND) {
-          reads(db + 1, a[(db + 1) & 1]);
-          asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(cur[0]), "+v"(cur[1]) : "n"(2 * NK));
-        } else {
-          asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(cur[0]), "+v"(cur[1]));
-        }
-#pragma unroll
-        for (int k16 = 0; k16 < NK; ++k16)
+        for (int k16 = 0; k16 < 2; ++k16)
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
-            oacc[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[k16], pb[nb][k16], oacc[db][nb], 0, 0, 0);
-      }
+            oacc[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][k16], pb[nb][k16], oacc[db][nb], 0, 0, 0);
+      });
     };
 
     // Software pipeline over the tile sequence, C::STAGES LDS stages in a
@@ -487,30 +507,30 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       n_tiles += x.vis;
     }
     Tile ld = first, nx = first;
-    if (n_tiles > 0) issue_loads(stage(Ic<0>{}), ld);
+    if (n_tiles > 0) issue_loads(Ic<0>{}, ld);
     ld = advance(ld);
     nx = ld;
-    if (n_tiles > 1) issue_loads(stage(Ic<1>{}), ld);
+    if (n_tiles > 1) issue_loads(Ic<1>{}, ld);
     ld = advance(ld);
-    if (n_tiles > 2) issue_loads(stage(Ic<2>{}), ld);
+    if (n_tiles > 2) issue_loads(Ic<2>{}, ld);
     ld = advance(ld);
     if constexpr (NS > 4) {
-      if (n_tiles > 3) issue_loads(stage(Ic<3>{}), ld);
+      if (n_tiles > 3) issue_loads(Ic<3>{}, ld);
       ld = advance(ld);
     }
     if constexpr (NS > 5 && !C::PAIRED) {
-      if (n_tiles > 4) issue_loads(stage(Ic<4>{}), ld);
+      if (n_tiles > 4) issue_loads(Ic<4>{}, ld);
       ld = advance(ld);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
     f32x16 xa[MB][NB], xb[MB][NB];
-    bf16x8 pb[NB][2 * MB];
+    bf16x8 pb[NB][2 * MB], va[D / 32][2 * MB];
     float mt[NB], ls[NB];
     bool unset = false;
     if (n_tiles > 0) {
-      qk(xa, stage(Ic<0>{}));
+      qk(xa, Ic<0>{});
       if (first.kt >= first.full) mask(xa, first);
       row_max(xa, mt);
       shift(xa);
@@ -528,17 +548,18 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       auto& y = (k % 2 == 0) ? xb : xa;
       const bool has_next = i + 1 < n_tiles;
       if constexpr (!C::PAIRED) {
-        if (i + NS - 1 < n_tiles) issue_loads(stage(Ic<(k + NS - 1) % NS>{}), ld);
+        if (i + NS - 1 < n_tiles) issue_loads(Ic<(k + NS - 1) % NS>{}, ld);
         ld = advance(ld);
       } else if constexpr (k % 2 == 0) {
         // Paired steps: tiles i+4 and i+5 refill the stages of tiles i-2 and
         // i-1, released by the barrier that closed step i-1.
-        if (i + 4 < n_tiles) issue_loads(stage(Ic<(k + 4) % NS>{}), ld);
+        if (i + 4 < n_tiles) issue_loads(Ic<(k + 4) % NS>{}, ld);
         ld = advance(ld);
-        if (i + 5 < n_tiles) issue_loads(stage(Ic<(k + 5) % NS>{}), ld);
+        if (i + 5 < n_tiles) issue_loads(Ic<(k + 5) % NS>{}, ld);
         ld = advance(ld);
       }
-      qk(y, stage(Ic<(k + 1) % NS>{}));  // harmless when there is no tile i+1
+      qk(y, Ic<(k + 1) % NS>{});  // harmless when there is no tile i+1
+      v_reads(Ic<k % NS>{}, va);
       exps(x, pb, ls);
       bool over = false;
 #pragma unroll
@@ -561,7 +582,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
         for (int k4 = 0; k4 < 2 * MB; ++k4) asm volatile("" : "+v"(pb[nb][k4]));
       if (has_next && nx.kt >= nx.full) mask(y, nx);
-      pv(stage(Ic<k % NS>{}), pb);
+      pv(va, pb);
       shift(y);
       // Keep the shift beside the value product (left alone, it sinks into
       // the next step, where the vector unit already has the exponentials).
