@@ -92,6 +92,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="s128k_c16_zigzag_16x1", choices=sorted(workloads.WORKLOAD_BY_NAME))
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle CPU-baseline budget (0: skip)")
+    ap.add_argument("--suite", action="store_true",
+                    help="instead of the headline line, print one JSON line per secondary measurement: "
+                         "MFMA probe, per-shard balance (32k tokens), warm/cold and overlap on/off "
+                         "(131k tokens), partial+merge and bidirectional passes (262k tokens)")
+    ap.add_argument("--reps", type=int, default=5, help="repetitions per timed launch in --suite")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the ring: run with --gpus 1 (got {args.gpus}); "
@@ -101,6 +106,9 @@ def main():
     import torch
     import ring_parallelism_amd as ra
 
+    if args.suite:
+        suite(args)
+        return
     w = workloads.WORKLOAD_BY_NAME[args.workload]
     dev = torch.device("cuda:0")
     in_dt = ra.BF16 if w.dtype == "bf16" else ra.F32
@@ -160,6 +168,13 @@ def main():
         torch.cuda.synchronize()
         kernel_ms.extend(ev[r][0].elapsed_time(ev[r][1]) for r in range(c))
 
+    # The box's sustained bf16 MFMA rate (same instruction mix, no memory
+    # traffic): context for the fraction of the published peak.
+    nwg, pflop = ra.ring_attn_mfma_probe(2000)
+    sink = torch.empty(nwg * 512, dtype=torch.float32, device=dev)
+    probe_ms = timed(torch, lambda: ra.ring_attn_mfma_probe(2000, sink), 3)
+    probe_tf = pflop / (float(np.median(probe_ms)) / 1e3) / 1e12
+
     pairs = [shard_pairs(w, r) for r in range(c)]               # per query head
     flop_step = sum(useful_flop(w, pr) for pr in pairs)
     pairs_counted = st[0] / args.steps
@@ -186,13 +201,169 @@ def main():
                      "traffic": measured_traffic() if w.name == "s128k_c16_zigzag_16x1" else None,
                      "kernel": "fwd_bf16_kernel" if w.dtype == "bf16" else "fwd_f32_kernel",
                      "flop_per_launch": flop_launch, "avg_launch_ms": round(avg_kernel_s * 1e3, 4),
-                     "launches_timed": len(kernel_ms)},
+                     "launches_timed": len(kernel_ms),
+                     "probe_sustained_tflops": round(probe_tf, 1),
+                     "frac_of_probe": round(achieved / probe_tf, 4)},
         "stats_per_step": {"pairs": int(pairs_counted), "tiles_full": st[1] // args.steps,
                            "tiles_partial": st[2] // args.steps, "tiles_skipped": st[3] // args.steps},
     }
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def emit(d):
+    print(json.dumps(d), flush=True)
+
+
+def device_inputs(w, torch, dev, blocks_for=None):
+    """Seeded synthetic Q shards and K/V blocks drawn on the device: N(0, sigma^2)
+    rounded to bf16, in shard layout [c, B, H, S/c, d] (timing inputs; the values
+    only matter through their distribution).  blocks_for: only Q of these shards."""
+    g = torch.Generator(device=dev).manual_seed(w.seed)
+    c, n = w.n_shards, w.n_loc
+    ranks = range(c) if blocks_for is None else blocks_for
+    qs = {r: (torch.randn((w.batch, w.h_q, n, w.head_dim), generator=g, device=dev) * w.sigma).to(torch.bfloat16)
+          for r in ranks}
+    ks = (torch.randn((c, w.batch, w.h_kv, n, w.head_dim), generator=g, device=dev) * w.sigma).to(torch.bfloat16)
+    vs = (torch.randn((c, w.batch, w.h_kv, n, w.head_dim), generator=g, device=dev) * w.sigma).to(torch.bfloat16)
+    return qs, ks, vs
+
+
+def timed(torch, fn, reps, scrub=None):
+    """Per-launch milliseconds of fn() from HIP events on the current stream;
+    with `scrub` (a large device tensor) the caches are flushed by a full
+    write of it before every launch."""
+    fn()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        if scrub is not None:
+            scrub.fill_(1.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    return ms
+
+
+def stat(ms):
+    return {"median_ms": round(float(np.median(ms)), 4), "min_ms": round(float(np.min(ms)), 4), "reps": len(ms)}
+
+
+def suite(args):
+    """Secondary measurements, one JSON line each (inputs resident in HBM)."""
+    import torch
+    import ring_parallelism_amd as ra
+    dev = torch.device("cuda:0")
+    reps = max(1, args.reps)
+
+    # Sustained bf16 MFMA rate of this device with the attention step's matrix mix.
+    nwg, flop = ra.ring_attn_mfma_probe(2000)
+    sink = torch.empty(nwg * 512, dtype=torch.float32, device=dev)
+    ms = timed(torch, lambda: ra.ring_attn_mfma_probe(2000, sink), reps)
+    tf = flop / (np.median(ms) / 1e3) / 1e12
+    emit({"measurement": "mfma_probe", "workgroups": nwg, "flop": flop, **stat(ms),
+          "tflops": round(tf, 1), "pct_of_nominal": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+          "implied_clock_ghz_at_4096_flop_per_clk_per_cu": round(tf * 1e12 / (nwg * 4096) / 1e9, 3)})
+
+    def fwd(w, desc, r, q, ks, vs, out, lse, owners=None):
+        c = w.n_shards
+        own = [(r - t) % c for t in range(c)] if owners is None else owners
+        return lambda: ra.ring_attn_shard_fwd(desc, r, q, [ks[j] for j in own], [vs[j] for j in own], out, lse,
+                                              block_owner=own)
+
+    # Per-shard work and time under the three placements (32 768 tokens, c = 16).
+    for name in ("s32k_c16_contig_16x1", "s32k_c16_zigzag_16x1", None):
+        if name is None:
+            w = workloads.WORKLOAD_BY_NAME["s32k_c16_zigzag_16x1"]
+            w = workloads.Workload(**{**w.__dict__, "name": "s32k_c16_striped_16x1", "split": workloads.SPLIT_STRIPED})
+        else:
+            w = workloads.WORKLOAD_BY_NAME[name]
+        qs, ks, vs = device_inputs(w, torch, dev)
+        out = torch.empty((w.batch, w.h_q, w.n_loc, w.head_dim), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((w.batch, w.h_q, w.n_loc), dtype=torch.float32, device=dev)
+        desc = ra.make_desc(w.seq_len, w.n_shards, w.split, w.batch, w.h_q, w.h_kv, w.head_dim, ra.BF16, ra.BF16,
+                            w.causal, w.scale)
+        med, flops = [], []
+        for r in range(w.n_shards):
+            m = stat(timed(torch, fwd(w, desc, r, qs[r], ks, vs, out, lse), reps))["median_ms"]
+            med.append(m)
+            flops.append(useful_flop(w, shard_pairs(w, r)))
+        work = [f / np.mean(flops) for f in flops]
+        emit({"measurement": "per_shard_balance", "workload": w.name,
+              "split": {0: "contiguous", 1: "zigzag", 2: "striped"}[w.split],
+              "shard_median_ms": med, "busiest_over_mean_time": round(max(med) / float(np.mean(med)), 4),
+              "busiest_over_mean_work": round(max(work), 4),
+              "max_over_min_time": round(max(med) / min(med), 4),
+              "total_ms": round(sum(med), 3),
+              "tflops_all_shards": round(sum(flops) / (sum(med) / 1e3) / 1e12, 1)})
+        del qs, ks, vs
+
+    # 131 072 tokens, shard 0: warm vs cold caches, loads overlapped vs not.
+    w = workloads.WORKLOAD_BY_NAME["s128k_c16_zigzag_16x1"]
+    qs, ks, vs = device_inputs(w, torch, dev, blocks_for=[0])
+    out = torch.empty((w.batch, w.h_q, w.n_loc, w.head_dim), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.batch, w.h_q, w.n_loc), dtype=torch.float32, device=dev)
+    f0 = useful_flop(w, shard_pairs(w, 0))
+    scrub = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+    for mode, flags, sc in (("warm", 0, None), ("cold", 0, scrub), ("warm_no_overlap", ra.FLAG_SYNC_LOADS, None)):
+        desc = ra.make_desc(w.seq_len, w.n_shards, w.split, w.batch, w.h_q, w.h_kv, w.head_dim, ra.BF16, ra.BF16,
+                            True, w.scale, flags)
+        st = stat(timed(torch, fwd(w, desc, 0, qs[0], ks, vs, out, lse), reps, sc))
+        emit({"measurement": "shard_pass", "workload": w.name, "mode": mode, **st,
+              "tflops": round(f0 / (st["median_ms"] / 1e3) / 1e12, 1)})
+    del qs, ks, vs, scrub
+
+    # 262 144 tokens, c = 32, 64/8 heads, shard 0: fused pass, per-block partials
+    # folded by 31 two-way merges, and the bidirectional (non-causal) pass.
+    w = workloads.WORKLOAD_BY_NAME["s256k_c32_zigzag_64x8"]
+    qs, ks, vs = device_inputs(w, torch, dev, blocks_for=[0])
+    c, n = w.n_shards, w.n_loc
+    out = torch.empty((w.batch, w.h_q, n, w.head_dim), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.batch, w.h_q, n), dtype=torch.float32, device=dev)
+    for causal in (True, False):
+        desc = ra.make_desc(w.seq_len, c, w.split, w.batch, w.h_q, w.h_kv, w.head_dim, ra.BF16, ra.BF16, causal,
+                            w.scale)
+        st = stat(timed(torch, fwd(w, desc, 0, qs[0], ks, vs, out, lse), reps))
+        fl = useful_flop(w, shard_pairs(w, 0)) if causal else 4.0 * w.head_dim * w.h_q * w.batch * n * w.seq_len
+        emit({"measurement": "shard_pass", "workload": w.name, "mode": "fused_causal" if causal else "fused_bidirectional",
+              **st, "tflops": round(fl / (st["median_ms"] / 1e3) / 1e12, 1)})
+    acc = torch.empty((w.batch, w.h_q, n, w.head_dim), dtype=torch.float32, device=dev)
+    acc_l = torch.empty((w.batch, w.h_q, n), dtype=torch.float32, device=dev)
+    part = torch.empty_like(acc)
+    part_l = torch.empty_like(acc_l)
+    pdesc = ra.make_desc(w.seq_len, c, w.split, w.batch, w.h_q, w.h_kv, w.head_dim, ra.BF16, ra.F32, True, w.scale)
+    merge_ms = []
+
+    def partial_merge(record):
+        for t in range(c):
+            j = (0 - t) % c
+            dst, dst_l = (acc, acc_l) if t == 0 else (part, part_l)
+            ra.ring_attn_shard_fwd(pdesc, 0, qs[0], [ks[j]], [vs[j]], dst, dst_l, block_owner=[j])
+            if t > 0:
+                if record:
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                ra.ring_attn_merge(w.batch, w.h_q, n, w.head_dim, [acc, part], ra.F32, [acc_l, part_l], acc, ra.F32,
+                                   acc_l)
+                if record:
+                    e1.record()
+                    merge_ms.append((e0, e1))
+
+    st = stat(timed(torch, lambda: partial_merge(False), reps))
+    partial_merge(True)
+    torch.cuda.synchronize()
+    mm = [a.elapsed_time(b) for a, b in merge_ms]
+    merge_bytes = 3 * (acc.numel() * 4 + acc_l.numel() * 4)
+    emit({"measurement": "partials_plus_merges", "workload": w.name, "partial_calls": c, "merges": c - 1, **st,
+          "tflops": round(useful_flop(w, shard_pairs(w, 0)) / (st["median_ms"] / 1e3) / 1e12, 1),
+          "merge_median_ms": round(float(np.median(mm)), 4), "merge_bytes": merge_bytes,
+          "merge_roofline": {"bound": "hbm", "achieved": round(merge_bytes / (np.median(mm) / 1e3) / 1e9, 1),
+                             "peak": 8000.0, "unit": "GB/s",
+                             "frac": round(merge_bytes / (np.median(mm) / 1e3) / 1e9 / 8000.0, 4)}})
 
 
 def shard_pairs(w, r):

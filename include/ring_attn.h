@@ -55,7 +55,7 @@ enum { RA_F32 = 0, RA_BF16 = 1 };
 
 #define RA_MAX_BLOCKS 128  /* ring blocks per ring_attn_shard_fwd call */
 #define RA_MAX_PARTS 64    /* partial results per ring_attn_merge call */
-#define RA_ABI_VERSION 1
+#define RA_ABI_VERSION 2
 
 typedef struct {
   int64_t seq_len;   /* S, global tokens; S % c == 0 (S % 2c == 0 for ZIGZAG) */
@@ -71,7 +71,16 @@ typedef struct {
   int32_t out_dtype; /* RA_F32 or RA_BF16; bf16 inputs may write fp32 out */
   int32_t causal;    /* 1: key position <= query position (global positions); 0: all keys */
   float scale;       /* softmax scale applied to q.k: finite and > 0 (e.g. 1/sqrt(d)) */
+  uint32_t flags;    /* RA_FLAG_* bits; 0 for normal use */
 } ra_attn_desc;
+
+/* Measurement switch for the "with and without overlap" comparison
+ * ("Sequence / context parallelism" notes, section 10, exercise C): the
+ * key/value tiles are still prefetched into the LDS ring, but every wave
+ * waits for each batch of tile loads right after issuing it, so the transfer
+ * no longer overlaps the attention arithmetic.  Results are bitwise the same.
+ * bf16 inputs only (RA_EUNSUPPORTED with fp32 inputs). */
+#define RA_FLAG_SYNC_LOADS 1u
 
 /* Shard placement and optional gather into shard-major order.
  *
@@ -163,6 +172,21 @@ const char* ring_attn_last_error(void);
 
 /* RA_ABI_VERSION of the loaded library. */
 int32_t ring_attn_abi_version(void);
+
+/* Calibration probe for the roofline: the matrix-core instruction mix of one
+ * attention step (a dependent chain of eight v_mfma_f32_32x32x16_bf16 and
+ * four chains of two, no memory traffic) run `iters` times by eight waves on
+ * every compute unit, so that the sustained bf16 MFMA rate (and hence the
+ * shader clock under matrix load) can be timed next to the attention kernel.
+ * Not part of the attention path.
+ *
+ * iters >= 1; sink (device float[*n_workgroups * 512], caller-owned) receives
+ * the accumulators so that the work is not optimised away.  On success
+ * *n_workgroups is the number of workgroups launched (the device's compute
+ * unit count) and *flop the dense FLOP the launch performs.  Passing sink =
+ * NULL only fills *n_workgroups and *flop (nothing is launched). */
+ra_status ring_attn_mfma_probe(int64_t iters, float* sink, int32_t* n_workgroups, double* flop,
+                               void* stream);
 
 #ifdef __cplusplus
 }

@@ -17,6 +17,7 @@ SPLIT_ZIGZAG = 1
 SPLIT_STRIPED = 2
 F32 = 0
 BF16 = 1
+FLAG_SYNC_LOADS = 1
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 MAX_BLOCKS = 128
 MAX_PARTS = 64
@@ -26,7 +27,7 @@ LIB_PATH = os.environ.get("RING_ATTN_LIB") or os.path.join(os.path.dirname(os.pa
                                                            "libring_attn.so")
 
 EXPORTS = ("zigzag_partition", "zigzag_unpartition", "ring_attn_shard_fwd", "ring_attn_tile_shape",
-           "ring_attn_merge", "ring_attn_last_error", "ring_attn_abi_version")
+           "ring_attn_merge", "ring_attn_last_error", "ring_attn_abi_version", "ring_attn_mfma_probe")
 
 
 class RingAttnError(RuntimeError):
@@ -48,6 +49,7 @@ class AttnDesc(ctypes.Structure):
         ("out_dtype", ctypes.c_int32),
         ("causal", ctypes.c_int32),
         ("scale", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
     ]
 
 
@@ -69,8 +71,9 @@ def lib():
     L.ring_attn_shard_fwd.argtypes = [ctypes.POINTER(AttnDesc), i32, vp, i32, vp, vp, vp, vp, vp, vp, vp]
     L.ring_attn_tile_shape.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.ring_attn_merge.argtypes = [i32, i32, i64, i32, i32, vp, i32, vp, vp, i32, vp, vp]
+    L.ring_attn_mfma_probe.argtypes = [i64, vp, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double), vp]
     for name in ("zigzag_partition", "zigzag_unpartition", "ring_attn_shard_fwd",
-                 "ring_attn_tile_shape", "ring_attn_merge"):
+                 "ring_attn_tile_shape", "ring_attn_merge", "ring_attn_mfma_probe"):
         getattr(L, name).restype = i32
     L.ring_attn_last_error.restype = ctypes.c_char_p
     L.ring_attn_abi_version.restype = i32
@@ -107,11 +110,12 @@ def abi_version() -> int:
 
 
 def make_desc(seq_len, n_shards, split, batch, h_q, h_kv, head_dim, in_dtype, out_dtype,
-              causal=True, scale=None) -> AttnDesc:
+              causal=True, scale=None, flags=0) -> AttnDesc:
     if scale is None:
         scale = head_dim ** -0.5
     return AttnDesc(int(seq_len), int(n_shards), int(split), int(batch), int(h_q), int(h_kv),
-                    int(head_dim), int(in_dtype), int(out_dtype), int(bool(causal)), float(scale))
+                    int(head_dim), int(in_dtype), int(out_dtype), int(bool(causal)), float(scale),
+                    int(flags))
 
 
 def zigzag_partition(seq_len, n_shards, split, perm=None, src=None, dst=None, outer=0,
@@ -162,6 +166,16 @@ def ring_attn_merge(batch, heads, rows, head_dim, outs, parts_dtype, lses, out, 
     _check(lib().ring_attn_merge(int(batch), int(heads), int(rows), int(head_dim), n, op,
                                  int(parts_dtype), lp, _ptr(out), int(out_dtype), _ptr(lse),
                                  _stream(stream, out, lse)))
+
+
+def ring_attn_mfma_probe(iters, sink=None, stream=None):
+    """Launch the matrix-core calibration probe (``sink``: device float32 tensor
+    of at least n_workgroups * 512 elements; None only queries).  Returns
+    ``(n_workgroups, flop)`` of the launch."""
+    nwg, flop = ctypes.c_int32(0), ctypes.c_double(0.0)
+    _check(lib().ring_attn_mfma_probe(int(iters), _ptr(sink), ctypes.byref(nwg), ctypes.byref(flop),
+                                      _stream(stream, sink)))
+    return int(nwg.value), float(flop.value)
 
 
 def shard_tensor(x, n_shards, split, stream=None):

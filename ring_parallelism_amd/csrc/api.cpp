@@ -60,6 +60,9 @@ ra_status check_desc(const ra_attn_desc* d) {
     return fail(RA_EUNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
   if (d->in_dtype == RA_F32 && d->out_dtype == RA_BF16)
     return fail(RA_EUNSUPPORTED, "fp32 inputs with bf16 output are not supported");
+  if ((d->flags & ~RA_FLAG_SYNC_LOADS) != 0) return fail(RA_EINVAL, "unknown flags 0x%x", d->flags);
+  if ((d->flags & RA_FLAG_SYNC_LOADS) && d->in_dtype != RA_BF16)
+    return fail(RA_EUNSUPPORTED, "RA_FLAG_SYNC_LOADS applies to bf16 inputs only");
   if (d->seq_len >= ((int64_t)1 << 31) - 1)
     return fail(RA_EUNSUPPORTED, "seq_len must be < 2^31 - 1 for attention");
   const int64_t n_loc = d->seq_len / d->n_shards;
@@ -178,6 +181,7 @@ ra_status ring_attn_shard_fwd(const ra_attn_desc* desc, int32_t rank, const void
   p.causal = desc->causal;
   p.scale = desc->scale;
   p.scale_log2 = (float)((double)desc->scale * 1.4426950408889634);
+  p.sync_loads = (desc->flags & RA_FLAG_SYNC_LOADS) ? 1 : 0;
 
   hipError_t e = desc->in_dtype == RA_F32
                      ? ra::launch_fwd_f32(p, desc->head_dim, (hipStream_t)stream)
@@ -225,6 +229,25 @@ ra_status ring_attn_merge(int32_t batch, int32_t heads, int64_t rows, int32_t he
   p.n_parts = n_parts;
   hipError_t e = ra::launch_merge(p, parts_dtype, out_dtype, (hipStream_t)stream);
   if (e != hipSuccess) return fail(RA_EHIP, "merge launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+
+ra_status ring_attn_mfma_probe(int64_t iters, float* sink, int32_t* n_workgroups, double* flop,
+                               void* stream) {
+  if (iters < 1) return fail(RA_EINVAL, "iters must be >= 1");
+  if (!n_workgroups || !flop) return fail(RA_EINVAL, "n_workgroups and flop must be set");
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return fail(RA_EHIP, "device query failed: %s", hipGetErrorString(e));
+  if (cus < 1) return fail(RA_EHIP, "device reports %d compute units", cus);
+  *n_workgroups = cus;
+  *flop = ra::mfma_probe_flop(iters, cus);
+  if (!sink) return ok();
+  if (!aligned(sink, 4)) return fail(RA_EINVAL, "sink must be 4-byte aligned");
+  e = ra::launch_mfma_probe(iters, sink, cus, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RA_EHIP, "probe launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

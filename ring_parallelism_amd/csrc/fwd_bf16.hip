@@ -557,6 +557,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
         ld = advance(ld);
         if (i + 5 < n_tiles) issue_loads(Ic<(k + 5) % NS>{}, ld);
         ld = advance(ld);
+        // Measurement mode: no overlap of the tile transfers with compute.
+        if (p.sync_loads) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
       qk(y, Ic<(k + 1) % NS>{});  // harmless when there is no tile i+1
       v_reads(Ic<k % NS>{}, va);

@@ -78,6 +78,7 @@ struct FwdParams {
   int32_t n_ktiles;    // ceil(n_loc / tile_k)
   float scale;         // softmax scale
   float scale_log2;    // scale * log2(e)
+  int32_t sync_loads;  // wait for each batch of tile loads right after issuing it
   int32_t owner[RA_MAX_BLOCKS];
   const void* k[RA_MAX_BLOCKS];
   const void* v[RA_MAX_BLOCKS];
@@ -104,5 +105,8 @@ hipError_t launch_merge(const MergeParams& p, int32_t parts_dtype, int32_t out_d
                         hipStream_t stream);
 void tile_shape_f32(int32_t head_dim, int32_t* tq, int32_t* tk);
 void tile_shape_bf16(int32_t head_dim, int32_t* tq, int32_t* tk);
+hipError_t launch_mfma_probe(int64_t iters, float* sink, int32_t n_workgroups, hipStream_t stream);
+constexpr int kProbeThreads = 512;  // eight waves per workgroup
+double mfma_probe_flop(int64_t iters, int32_t n_workgroups);
 
 }  // namespace ra

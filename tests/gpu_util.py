@@ -50,21 +50,21 @@ class Problem:
     def from_workload(cls, w):
         return cls(w.seq_len, w.n_shards, w.split, w.batch, w.h_q, w.h_kv, w.head_dim, w.dtype, w.sigma, w.seed)
 
-    def desc(self, out_dtype=ra.F32, causal=True):
+    def desc(self, out_dtype=ra.F32, causal=True, flags=0):
         in_dt = ra.BF16 if self.dtype == "bf16" else ra.F32
         return ra.make_desc(self.S, self.c, self.split, self.B, self.Hq, self.Hkv, self.d, in_dt,
-                            out_dtype, causal, self.scale)
+                            out_dtype, causal, self.scale, flags)
 
     def ring_owners(self, rank):
         return [(rank - t) % self.c for t in range(self.c)]
 
-    def run(self, rank, out_dtype=ra.F32, causal=True, owners=None, with_stats=True, fill=float("nan")):
+    def run(self, rank, out_dtype=ra.F32, causal=True, owners=None, with_stats=True, fill=float("nan"), flags=0):
         owners = self.ring_owners(rank) if owners is None else list(owners)
         odt = torch.float32 if out_dtype == ra.F32 else torch.bfloat16
         out = torch.full((self.B, self.Hq, self.n_loc, self.d), fill, dtype=odt, device=DEV)
         lse = torch.full((self.B, self.Hq, self.n_loc), fill, dtype=torch.float32, device=DEV)
         stats = torch.zeros(4, dtype=torch.int64, device=DEV) if with_stats else None
-        ra.ring_attn_shard_fwd(self.desc(out_dtype, causal), rank, self.qs[rank],
+        ra.ring_attn_shard_fwd(self.desc(out_dtype, causal, flags), rank, self.qs[rank],
                                [self.ks[j] for j in owners], [self.vs[j] for j in owners],
                                out, lse, block_owner=owners, stats=stats)
         torch.cuda.synchronize()

@@ -9,7 +9,8 @@ import pytest
 
 import ring_parallelism_amd as ra
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ring_attn.h")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ring_attn.h")
 FAKE = 0x10000  # 64 KiB-aligned fake device address; never dereferenced by a failing call
 
 
@@ -25,7 +26,27 @@ def test_library_exports_every_declared_symbol():
     lib = ra.lib()
     for n in names:
         assert hasattr(lib, n), n
-    assert ra.abi_version() == 1
+    header = open(os.path.join(ROOT, "include", "ring_attn.h")).read()
+    assert ra.abi_version() == int(re.search(r"#define RA_ABI_VERSION (\d+)", header).group(1))
+
+
+def test_descriptor_layout_matches_c(tmp_path):
+    """The ctypes mirror of ra_attn_desc has the C struct's size and offsets."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no host C compiler")
+    fields = [f[0] for f in ra.AttnDesc._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "ring_attn.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(ra_attn_desc));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(ra_attn_desc, {f}));\n' for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(ra.AttnDesc)
+    assert got[1:] == [getattr(ra.AttnDesc, f).offset for f in fields]
 
 
 def good_desc(**kw):
@@ -33,7 +54,8 @@ def good_desc(**kw):
              in_dtype=ra.BF16, out_dtype=ra.F32, causal=True, scale=128 ** -0.5)
     d.update(kw)
     return ra.AttnDesc(d["seq_len"], d["n_shards"], d["split"], d["batch"], d["h_q"], d["h_kv"],
-                       d["head_dim"], d["in_dtype"], d["out_dtype"], int(d["causal"]), d["scale"])
+                       d["head_dim"], d["in_dtype"], d["out_dtype"], int(d["causal"]), d["scale"],
+                       d.get("flags", 0))
 
 
 def expect(status, fn, *a, match=None, **kw):
@@ -67,6 +89,8 @@ def test_tile_shape():
     (dict(scale=0.0), ra.EINVAL, "scale"),
     (dict(scale=float("nan")), ra.EINVAL, "scale"),
     (dict(seq_len=1 << 31, n_shards=2), ra.EUNSUPPORTED, "2\\^31"),
+    (dict(flags=2), ra.EINVAL, "flags"),
+    (dict(flags=ra.FLAG_SYNC_LOADS, in_dtype=ra.F32), ra.EUNSUPPORTED, "bf16 inputs only"),
 ])
 def test_descriptor_validation(kw, status, match):
     expect(status, ra.ring_attn_tile_shape, good_desc(**kw), match=match)
@@ -157,3 +181,9 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(ra, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(ImportError):
         ra.lib()
+
+
+def test_mfma_probe_validation():
+    expect(ra.EINVAL, ra.ring_attn_mfma_probe, 0, match="iters")
+    L = ra.lib()
+    assert L.ring_attn_mfma_probe(1, None, None, None, None) == ra.EINVAL

@@ -98,6 +98,26 @@ def test_deterministic_and_writes_every_row():
     assert torch.isfinite(o1).all() and torch.isfinite(l1).all()
 
 
+def test_sync_loads_flag_is_bitwise_neutral():
+    """The no-overlap measurement mode only changes when loads are awaited."""
+    p = Problem(8192, 4, ra.SPLIT_ZIGZAG, 1, 4, 1, 128, "bf16", seed=17)
+    for r in (0, 3):
+        say(f"sync loads rank {r}")
+        o1, l1, s1 = p.run(r)
+        o2, l2, s2 = p.run(r, flags=ra.FLAG_SYNC_LOADS, fill=0.0)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(s1, s2)
+
+
+def test_mfma_probe_runs():
+    nwg, flop = ra.ring_attn_mfma_probe(4)
+    assert nwg >= 1 and flop == 2.0 * 32 * 32 * 16 * 16 * 4 * 8 * nwg
+    sink = torch.full((nwg * 512,), float("nan"), dtype=torch.float32, device=DEV)
+    say("mfma probe")
+    assert ra.ring_attn_mfma_probe(4, sink) == (nwg, flop)
+    torch.cuda.synchronize()
+    assert torch.isfinite(sink).all()
+
+
 # ---------------------------------------------------------------- partial results and merge
 
 @pytest.mark.parametrize("dtype,split", [("bf16", ra.SPLIT_ZIGZAG), ("f32", ra.SPLIT_CONTIGUOUS), ("bf16", ra.SPLIT_CONTIGUOUS)])
