@@ -6,10 +6,11 @@
 // whose parts are all -inf yields (0, -inf).
 //
 // HBM-bound: each thread owns 4 consecutive elements of one row (16-byte fp32
-// or 8-byte bf16 accesses), consecutive threads walk a row and then the next
-// row, so every wavefront reads and writes contiguous memory.  The per-row
-// weights are recomputed by each of the row's threads from the n lse values
-// (a few scalars, cached).
+// or 8-byte bf16 accesses) and consecutive threads cover consecutive memory,
+// so every wavefront reads and writes contiguous bytes.  The parts are folded
+// in one pass with a running max (the weights of earlier parts are rescaled
+// when a later lse is larger), so each part's data and lse are loaded
+// together and nothing waits on a separate max pass.
 #include "ra_common.h"
 
 namespace ra {
@@ -42,55 +43,60 @@ __device__ inline void store4(void* base, int64_t idx, float4 x) {
 }
 
 template <typename PartT, typename OutT>
-__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
-  const int per_row = p.head_dim / 4;
-  const int64_t total = p.n_rows * per_row;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total; u += stride) {
-    const int64_t r = u / per_row;
-    const int64_t idx = r * p.head_dim + (u % per_row) * 4;
-    float mx = -INFINITY;
-    for (int k = 0; k < p.n_parts; ++k) mx = fmaxf(mx, p.lses[k][r]);
-    float4 acc = {0.f, 0.f, 0.f, 0.f};
-    float z = 0.f;
-    if (mx != -INFINITY) {
-      for (int k = 0; k < p.n_parts; ++k) {
-        const float w = expf(p.lses[k][r] - mx);  // exp(-inf) = 0
-        z += w;
-        if (w != 0.f) {
-          const float4 o = load4<PartT>(p.outs[k], idx);
-          acc.x = fmaf(w, o.x, acc.x);
-          acc.y = fmaf(w, o.y, acc.y);
-          acc.z = fmaf(w, o.z, acc.z);
-          acc.w = fmaf(w, o.w, acc.w);
-        }
-      }
+__global__ __launch_bounds__(256) void merge_kernel(MergeParams p, int row_shift, int64_t total) {
+  const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // 4-element group
+  if (u >= total) return;
+  const int64_t r = u >> row_shift;  // head_dim / 4 groups per row (a power of two)
+  const int64_t idx = u * 4;
+  float m = -INFINITY, z = 0.f;
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < p.n_parts; ++k) {
+    const float l = p.lses[k][r];
+    const float4 o = load4<PartT>(p.outs[k], idx);
+    if (l == -INFINITY) continue;  // no keys in this part (its out is not read)
+    if (l > m) {
+      const float s = expf(m - l);  // 0 while m = -inf
+      acc.x *= s;
+      acc.y *= s;
+      acc.z *= s;
+      acc.w *= s;
+      z *= s;
+      m = l;
     }
-    const float inv = z > 0.f ? 1.f / z : 0.f;
-    // Every thread of the row has read its inputs before any write: a thread
-    // only ever writes the elements it read, so out/lse may alias part 0.
-    store4<OutT>(p.out, idx, float4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv});
-    if (u % per_row == 0) p.lse[r] = z > 0.f ? mx + logf(z) : -INFINITY;
+    const float w = expf(l - m);
+    z += w;
+    acc.x = fmaf(w, o.x, acc.x);
+    acc.y = fmaf(w, o.y, acc.y);
+    acc.z = fmaf(w, o.z, acc.z);
+    acc.w = fmaf(w, o.w, acc.w);
   }
+  const float inv = z > 0.f ? 1.f / z : 0.f;
+  // A thread writes only the elements (and lse) it has read, so out/lse may
+  // alias part 0.
+  store4<OutT>(p.out, idx, float4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv});
+  if ((u & ((1 << row_shift) - 1)) == 0) p.lse[r] = z > 0.f ? m + logf(z) : -INFINITY;
 }
 
 }  // namespace
 
 hipError_t launch_merge(const MergeParams& p, int32_t parts_dtype, int32_t out_dtype,
                         hipStream_t stream) {
-  const int64_t total = p.n_rows * (p.head_dim / 4);
-  int64_t grid = (total + 255) / 256;
-  if (grid > 256 * 64) grid = 256 * 64;
-  if (grid < 1) grid = 1;
+  const int per_row = p.head_dim / 4;  // a power of two (head_dim is a multiple of 4 dividing 256)
+  int shift = 0;
+  while ((1 << shift) < per_row) ++shift;
+  if ((1 << shift) != per_row) return hipErrorInvalidValue;
+  const int64_t total = p.n_rows * per_row;
+  const int64_t grid = (total + 255) / 256;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 gd((unsigned)grid), bd(256);
   if (parts_dtype == RA_F32 && out_dtype == RA_F32)
-    hipLaunchKernelGGL((merge_kernel<float, float>), gd, bd, 0, stream, p);
+    hipLaunchKernelGGL((merge_kernel<float, float>), gd, bd, 0, stream, p, shift, total);
   else if (parts_dtype == RA_F32)
-    hipLaunchKernelGGL((merge_kernel<float, __bf16>), gd, bd, 0, stream, p);
+    hipLaunchKernelGGL((merge_kernel<float, __bf16>), gd, bd, 0, stream, p, shift, total);
   else if (out_dtype == RA_F32)
-    hipLaunchKernelGGL((merge_kernel<__bf16, float>), gd, bd, 0, stream, p);
+    hipLaunchKernelGGL((merge_kernel<__bf16, float>), gd, bd, 0, stream, p, shift, total);
   else
-    hipLaunchKernelGGL((merge_kernel<__bf16, __bf16>), gd, bd, 0, stream, p);
+    hipLaunchKernelGGL((merge_kernel<__bf16, __bf16>), gd, bd, 0, stream, p, shift, total);
   return hipGetLastError();
 }
 
