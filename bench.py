@@ -317,6 +317,8 @@ def suite(args):
               "tflops": round(f0 / (st["median_ms"] / 1e3) / 1e12, 1)})
     del qs, ks, vs, scrub
 
+    decode_suite(torch, ra, dev, reps)
+
     # 262 144 tokens, c = 32, 64/8 heads, shard 0: fused pass, per-block partials
     # folded by 31 two-way merges, and the bidirectional (non-causal) pass.
     w = workloads.WORKLOAD_BY_NAME["s256k_c32_zigzag_64x8"]
@@ -364,6 +366,38 @@ def suite(args):
           "merge_roofline": {"bound": "hbm", "achieved": round(merge_bytes / (np.median(mm) / 1e3) / 1e9, 1),
                              "peak": 8000.0, "unit": "GB/s",
                              "frac": round(merge_bytes / (np.median(mm) / 1e3) / 1e9 / 8000.0, 4)}})
+
+
+def decode_suite(torch, ra, dev, reps):
+    """Split-KV decode of the 262 144-token cache (c = 32 blocks, 64/8 heads):
+    one query token per head, each block's keys in n_splits ranges, partials
+    folded by one strided merge.  HBM-bound: K and V are read once."""
+    w = workloads.WORKLOAD_BY_NAME["s256k_c32_zigzag_64x8"]
+    _, ks, vs = device_inputs(w, torch, dev, blocks_for=[])
+    g = torch.Generator(device=dev).manual_seed(w.seed + 1)
+    q = (torch.randn((w.batch, w.h_q, w.head_dim), generator=g, device=dev) * w.sigma).to(torch.bfloat16)
+    desc = ra.make_desc(w.seq_len, w.n_shards, w.split, w.batch, w.h_q, w.h_kv, w.head_dim, ra.BF16, ra.F32, True,
+                        w.scale)
+    kv_bytes = 2 * ks.numel() * ks.element_size()
+    for n_splits in (4, 8, 16):
+        n_parts = w.n_shards * n_splits
+        outs = torch.empty((n_parts, w.batch, w.h_q, w.head_dim), dtype=torch.float32, device=dev)
+        lses = torch.empty((n_parts, w.batch, w.h_q), dtype=torch.float32, device=dev)
+        out = torch.empty((w.batch, w.h_q, w.head_dim), dtype=torch.float32, device=dev)
+        lse = torch.empty((w.batch, w.h_q), dtype=torch.float32, device=dev)
+        blocks_k, blocks_v = list(ks), list(vs)
+        dec = lambda: ra.ring_attn_decode(desc, q, blocks_k, blocks_v, n_splits, outs, lses)  # noqa: E731
+        mrg = lambda: ra.ring_attn_merge_strided(w.batch, w.h_q, 1, w.head_dim, outs, ra.F32, lses, out,  # noqa: E731
+                                                 ra.F32, lse)
+        sd = stat(timed(torch, dec, reps))
+        sm = stat(timed(torch, mrg, reps))
+        st = stat(timed(torch, lambda: (dec(), mrg()), reps))
+        byts = kv_bytes + q.numel() * 2 + outs.numel() * 4 + lses.numel() * 4
+        gbs = byts / (sd["median_ms"] / 1e3) / 1e9
+        emit({"measurement": "split_kv_decode", "workload": "decode of " + w.name, "n_splits": n_splits,
+              "partials": n_parts, "decode": sd, "merge": sm, "decode_plus_merge": st,
+              "decode_roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                                  "frac": round(gbs / 8000.0, 4), "bytes": byts}})
 
 
 def shard_pairs(w, r):

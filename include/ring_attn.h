@@ -167,6 +167,41 @@ ra_status ring_attn_merge(int32_t batch, int32_t heads, int64_t rows, int32_t he
                           const float* const* lses, void* out, int32_t out_dtype, float* lse,
                           void* stream);
 
+/* ring_attn_merge with the parts in one buffer: part k's out starts
+ * out_stride elements after part k-1's (parts_dtype elements, out_stride >=
+ * batch*heads*rows*head_dim) and its lse lse_stride values after part k-1's
+ * (lse_stride >= batch*heads*rows).  Any n_parts >= 1.  out / lse may be part
+ * 0 exactly and must not overlap any other part.  Same formula, alignment
+ * (outs and out_stride keep 4-element groups aligned) and errors as
+ * ring_attn_merge. */
+ra_status ring_attn_merge_strided(int32_t batch, int32_t heads, int64_t rows, int32_t head_dim,
+                                  int32_t n_parts, const void* outs, int64_t out_stride, int32_t parts_dtype,
+                                  const float* lses, int64_t lse_stride, void* out, int32_t out_dtype,
+                                  float* lse, void* stream);
+
+/* Split-KV decode ("Sequence / context parallelism" notes, section 7: decode
+ * has one query, and attention over a key/value cache spread across devices
+ * is a split-K with a gather of partial results; section 9, pitfalls: decode
+ * gains less from sequence parallelism than prefill).
+ *
+ * q: [B, h_q, d] bf16, one new token per (sequence, query head), placed after
+ *   every cached key, so every key is visible (desc->causal changes nothing).
+ * k_blocks / v_blocks: host arrays of n_blocks device pointers (1 <= n_blocks
+ *   <= min(n_shards, RA_MAX_BLOCKS)), each a cache block [B, h_kv, S/c, d]
+ *   bf16 -- on a ring, the blocks a device holds.
+ * n_splits: each block's S/c keys are cut into n_splits ranges of
+ *   floor/ceil((S/c)/n_splits) keys (1 <= n_splits <= S/c).
+ * out_parts: [n_blocks * n_splits, B, h_q, d] fp32 and lse_parts:
+ *   [n_blocks * n_splits, B, h_q] fp32 (natural log) receive one partial per
+ *   (block t, range s) at index t * n_splits + s: the attention of the query
+ *   over that range's keys alone.  Fold them with ring_attn_merge_strided
+ *   (out_stride = B*h_q*d, lse_stride = B*h_q) into the full result.
+ * desc: in_dtype RA_BF16, out_dtype RA_F32 (the partials), flags 0,
+ *   h_q / h_kv <= 32 (RA_EUNSUPPORTED otherwise); split is not used. */
+ra_status ring_attn_decode(const ra_attn_desc* desc, const void* q, int32_t n_blocks,
+                           const void* const* k_blocks, const void* const* v_blocks, int32_t n_splits,
+                           float* out_parts, float* lse_parts, void* stream);
+
 /* Message for the last non-OK status returned on this thread. */
 const char* ring_attn_last_error(void);
 

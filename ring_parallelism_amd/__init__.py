@@ -27,7 +27,8 @@ LIB_PATH = os.environ.get("RING_ATTN_LIB") or os.path.join(os.path.dirname(os.pa
                                                            "libring_attn.so")
 
 EXPORTS = ("zigzag_partition", "zigzag_unpartition", "ring_attn_shard_fwd", "ring_attn_tile_shape",
-           "ring_attn_merge", "ring_attn_last_error", "ring_attn_abi_version", "ring_attn_mfma_probe")
+           "ring_attn_merge", "ring_attn_last_error", "ring_attn_abi_version", "ring_attn_mfma_probe",
+           "ring_attn_merge_strided", "ring_attn_decode")
 
 
 class RingAttnError(RuntimeError):
@@ -72,8 +73,11 @@ def lib():
     L.ring_attn_tile_shape.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.ring_attn_merge.argtypes = [i32, i32, i64, i32, i32, vp, i32, vp, vp, i32, vp, vp]
     L.ring_attn_mfma_probe.argtypes = [i64, vp, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double), vp]
+    L.ring_attn_merge_strided.argtypes = [i32, i32, i64, i32, i32, vp, i64, i32, vp, i64, vp, i32, vp, vp]
+    L.ring_attn_decode.argtypes = [ctypes.POINTER(AttnDesc), vp, i32, vp, vp, i32, vp, vp, vp]
     for name in ("zigzag_partition", "zigzag_unpartition", "ring_attn_shard_fwd",
-                 "ring_attn_tile_shape", "ring_attn_merge", "ring_attn_mfma_probe"):
+                 "ring_attn_tile_shape", "ring_attn_merge", "ring_attn_mfma_probe",
+                 "ring_attn_merge_strided", "ring_attn_decode"):
         getattr(L, name).restype = i32
     L.ring_attn_last_error.restype = ctypes.c_char_p
     L.ring_attn_abi_version.restype = i32
@@ -166,6 +170,29 @@ def ring_attn_merge(batch, heads, rows, head_dim, outs, parts_dtype, lses, out, 
     _check(lib().ring_attn_merge(int(batch), int(heads), int(rows), int(head_dim), n, op,
                                  int(parts_dtype), lp, _ptr(out), int(out_dtype), _ptr(lse),
                                  _stream(stream, out, lse)))
+
+
+def ring_attn_merge_strided(batch, heads, rows, head_dim, outs, parts_dtype, lses, out, out_dtype, lse,
+                            n_parts=None, out_stride=None, lse_stride=None, stream=None):
+    """Fold the parts stacked along the first dimension of ``outs`` / ``lses``
+    (strides default to one part's size); ``out``/``lse`` may be part 0."""
+    n = int(outs.shape[0]) if n_parts is None else int(n_parts)
+    os_ = batch * heads * rows * head_dim if out_stride is None else out_stride
+    ls_ = batch * heads * rows if lse_stride is None else lse_stride
+    _check(lib().ring_attn_merge_strided(int(batch), int(heads), int(rows), int(head_dim), n, _ptr(outs),
+                                         int(os_), int(parts_dtype), _ptr(lses), int(ls_), _ptr(out),
+                                         int(out_dtype), _ptr(lse), _stream(stream, out, lse)))
+
+
+def ring_attn_decode(desc, q, k_blocks, v_blocks, n_splits, out_parts, lse_parts, stream=None):
+    """Split-KV decode partials: one per (block, key range), at index block * n_splits + range."""
+    n = len(k_blocks)
+    if len(v_blocks) != n:
+        raise ValueError("k_blocks and v_blocks differ in length")
+    kp = (ctypes.c_void_p * max(n, 1))(*[_ptr(t) for t in k_blocks])
+    vp = (ctypes.c_void_p * max(n, 1))(*[_ptr(t) for t in v_blocks])
+    _check(lib().ring_attn_decode(ctypes.byref(desc), _ptr(q), n, kp, vp, int(n_splits), _ptr(out_parts),
+                                  _ptr(lse_parts), _stream(stream, q, out_parts)))
 
 
 def ring_attn_mfma_probe(iters, sink=None, stream=None):

@@ -251,4 +251,103 @@ ra_status ring_attn_mfma_probe(int64_t iters, float* sink, int32_t* n_workgroups
   return ok();
 }
 
+ra_status ring_attn_merge_strided(int32_t batch, int32_t heads, int64_t rows, int32_t head_dim,
+                                  int32_t n_parts, const void* outs, int64_t out_stride, int32_t parts_dtype,
+                                  const float* lses, int64_t lse_stride, void* out, int32_t out_dtype,
+                                  float* lse, void* stream) {
+  if (batch < 1 || heads < 1 || rows < 1 || head_dim < 1)
+    return fail(RA_EINVAL, "batch, heads, rows and head_dim must be >= 1");
+  if (n_parts < 1) return fail(RA_EINVAL, "n_parts must be >= 1");
+  if ((parts_dtype != RA_F32 && parts_dtype != RA_BF16) || (out_dtype != RA_F32 && out_dtype != RA_BF16))
+    return fail(RA_EINVAL, "unknown dtype");
+  if (head_dim % 4 != 0 || 256 % head_dim != 0)
+    return fail(RA_EUNSUPPORTED, "head_dim %d must be a multiple of 4 dividing 256", head_dim);
+  const int64_t n_rows = (int64_t)batch * heads * rows;
+  if (n_rows / rows != (int64_t)batch * heads || n_rows > ((int64_t)1 << 40))
+    return fail(RA_EINVAL, "batch * heads * rows too large");
+  if (!outs || !lses || !out || !lse) return fail(RA_EINVAL, "outs, lses, out and lse must be set");
+  if (out_stride < n_rows * head_dim || lse_stride < n_rows)
+    return fail(RA_EINVAL, "strides must be at least one part (%lld elements / %lld lse values)",
+                (long long)(n_rows * head_dim), (long long)n_rows);
+  if (out_stride > ((int64_t)1 << 46) / n_parts || lse_stride > ((int64_t)1 << 46) / n_parts)
+    return fail(RA_EINVAL, "part strides too large");
+  const int64_t pes = parts_dtype == RA_F32 ? 4 : 2, oes = out_dtype == RA_F32 ? 4 : 2;
+  if (!aligned(outs, 4 * pes) || (out_stride * pes) % (4 * pes) != 0 || !aligned(lses, 4))
+    return fail(RA_EINVAL, "parts misaligned (outs and out_stride must keep 4-element groups aligned)");
+  if (!aligned(out, 4 * oes) || !aligned(lse, 4)) return fail(RA_EINVAL, "out / lse misaligned");
+  // The output may be part 0 exactly; it must not overlap any other part.
+  const char* p0 = (const char*)outs;
+  const char* pend = p0 + (n_parts - 1) * out_stride * pes + n_rows * head_dim * pes;
+  const char* o0 = (const char*)out;
+  const char* oend = o0 + n_rows * head_dim * oes;
+  if (o0 != p0 && o0 < pend && oend > p0) return fail(RA_EINVAL, "out overlaps the parts other than part 0");
+  const char* l0 = (const char*)lses;
+  const char* lend = l0 + ((n_parts - 1) * lse_stride + n_rows) * 4;
+  if ((const char*)lse != l0 && (const char*)lse < lend && (const char*)(lse + n_rows) > l0)
+    return fail(RA_EINVAL, "lse overlaps the parts other than part 0");
+  if (o0 == p0 && parts_dtype != out_dtype) return fail(RA_EINVAL, "in-place merge needs parts_dtype == out_dtype");
+  ra::MergeParams p;
+  std::memset(&p, 0, sizeof p);
+  p.strided = 1;
+  p.outs_base = outs;
+  p.lses_base = lses;
+  p.out_stride = out_stride;
+  p.lse_stride = lse_stride;
+  p.out = out;
+  p.lse = lse;
+  p.n_rows = n_rows;
+  p.head_dim = head_dim;
+  p.n_parts = n_parts;
+  hipError_t e = ra::launch_merge(p, parts_dtype, out_dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RA_EHIP, "merge launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+ra_status ring_attn_decode(const ra_attn_desc* desc, const void* q, int32_t n_blocks,
+                           const void* const* k_blocks, const void* const* v_blocks, int32_t n_splits,
+                           float* out_parts, float* lse_parts, void* stream) {
+  ra_status st = check_desc(desc);
+  if (st != RA_OK) return st;
+  if (desc->in_dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "decode takes bf16 inputs");
+  if (desc->out_dtype != RA_F32) return fail(RA_EUNSUPPORTED, "decode partials are fp32 (out_dtype RA_F32)");
+  if (desc->flags != 0) return fail(RA_EINVAL, "decode takes no flags");
+  const int32_t group = desc->h_q / desc->h_kv;
+  if (group > 32) return fail(RA_EUNSUPPORTED, "h_q / h_kv = %d > 32 query heads per kv head", group);
+  const int32_t c = desc->n_shards;
+  if (n_blocks < 1 || n_blocks > c || n_blocks > RA_MAX_BLOCKS)
+    return fail(RA_EINVAL, "n_blocks %d not in [1, min(n_shards, %d)]", n_blocks, RA_MAX_BLOCKS);
+  const int64_t n_loc = desc->seq_len / c;
+  if (n_splits < 1 || n_splits > n_loc) return fail(RA_EINVAL, "n_splits %d not in [1, %lld]", n_splits, (long long)n_loc);
+  if (!q || !k_blocks || !v_blocks || !out_parts || !lse_parts)
+    return fail(RA_EINVAL, "q, k_blocks, v_blocks, out_parts and lse_parts must be set");
+  if (!aligned(q, 16) || !aligned(out_parts, 16) || !aligned(lse_parts, 4))
+    return fail(RA_EINVAL, "q / out_parts must be 16-byte aligned, lse_parts 4-byte");
+  const int64_t items = (int64_t)n_blocks * n_splits * desc->batch * desc->h_kv;
+  if (items >= ((int64_t)1 << 31)) return fail(RA_EUNSUPPORTED, "too many (block, range, batch, kv head) items");
+  ra::DecodeParams p;
+  std::memset(&p, 0, sizeof p);
+  for (int t = 0; t < n_blocks; ++t) {
+    if (!k_blocks[t] || !v_blocks[t]) return fail(RA_EINVAL, "k_blocks[%d] / v_blocks[%d] is NULL", t, t);
+    if (!aligned(k_blocks[t], 16) || !aligned(v_blocks[t], 16))
+      return fail(RA_EINVAL, "k_blocks[%d] / v_blocks[%d] must be 16-byte aligned", t, t);
+    p.k[t] = k_blocks[t];
+    p.v[t] = v_blocks[t];
+  }
+  p.q = q;
+  p.out_parts = out_parts;
+  p.lse_parts = lse_parts;
+  p.n_loc = n_loc;
+  p.n_blocks = n_blocks;
+  p.n_splits = n_splits;
+  p.batch = desc->batch;
+  p.h_q = desc->h_q;
+  p.h_kv = desc->h_kv;
+  p.group = group;
+  p.n_items = (int32_t)items;
+  p.scale_log2 = (float)((double)desc->scale * 1.4426950408889634);
+  hipError_t e = ra::launch_decode_bf16(p, desc->head_dim, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RA_EHIP, "decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

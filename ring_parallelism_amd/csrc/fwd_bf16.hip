@@ -45,6 +45,7 @@
 #include <type_traits>
 
 #include "ra_common.h"
+#include "tile_common.h"
 
 // Tile configuration: waves per workgroup, 32-row query blocks per wave,
 // 32-key blocks per pipeline step.  (Compile-time knobs for tuning sweeps.)
@@ -67,61 +68,9 @@
 namespace ra {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) char lds_char;
-
 // Largest 16-term in-lane sum of exponentials accepted without raising the
 // reference (each term is then <= 2^16).
 constexpr float kSumLimit = 65536.0f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
-
-// Combine a value across the two half-waves (lanes l and l ^ 32).  The swap
-// returns the pair {own, partner} (in an order that depends on the half), so
-// max and sum of the pair are the same in both halves, bit for bit.
-__device__ inline float halves_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ inline float halves_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// 16 bytes per lane from a buffer resource straight into LDS: lane i's data
-// lands at dst + 16 * i (dst is wave-uniform); the byte offset is the lane's
-// voff plus the wave-uniform soff, and out-of-range offsets read 0.
-// Kept as a plain device function: the host pass of a kernel template that
-// names this builtin directly emits no launch stub.
-__device__ inline void lds_load16(__amdgpu_buffer_rsrc_t r, lds_char* dst, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
-}
-
-template <int V>
-using Ic = std::integral_constant<int, V>;
-
-// Calls f(Ic<I>), f(Ic<I+1>), ..., f(Ic<N-1>) while each call returns true.
-template <int I, int N, typename F>
-__device__ inline bool unrolled_steps(F& f) {
-  if constexpr (I == N) {
-    return true;
-  } else {
-    if (!f(Ic<I>{})) return false;
-    return unrolled_steps<I + 1, N>(f);
-  }
-}
-
-// Calls f(Ic<I>), ..., f(Ic<N-1>).
-template <int I, int N, typename F>
-__device__ inline void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(Ic<I>{});
-    static_for<I + 1, N>(f);
-  }
-}
 
 template <int D, int NW, int NB, int MB>
 struct Cfg {
@@ -141,14 +90,8 @@ struct Cfg {
   static_assert(LOADS >= 1 && TILEB % (1024 * NW) == 0, "tile must split evenly over waves");
   static_assert(D == 64 || D == 128, "head_dim");
 
-  // 16-byte slot holding chunk c of tile row r (an involution in c).
-  // K: rows r..r+15 read at one chunk land in 16 different slots.
-  __device__ static int k_slot(int r, int c) { return c ^ (r & (CHUNKS - 1)); }
-  // V: the transposing reads of a half-wave touch rows r..r+3 (4 chunks each
-  // for d = 128); moving each row's chunk group keeps them apart.
-  __device__ static int v_slot(int r, int c) {
-    return D == 128 ? c ^ ((r & 3) << 2) : c ^ (((r >> 1) & 1) << 2);
-  }
+  __device__ static int k_slot(int r, int c) { return Swizzle<D>::k_slot(r, c); }
+  __device__ static int v_slot(int r, int c) { return Swizzle<D>::v_slot(r, c); }
 };
 
 template <int D, int NW, int NB, int MB, typename OutT>
@@ -186,7 +129,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
   const int n_loc = (int)p.n_loc;
   const int64_t kv_off = ((int64_t)b * p.h_kv + hk) * n_loc * D;
   const int64_t q_off = ((int64_t)b * p.h_q + h) * n_loc;
-  const int kv_bytes = n_loc * C::ROWB;  // one (batch, kv head) slice of a block
+  // Bytes of one (batch, kv head) slice of a block (< 2^32: n_loc * d < 2^31).
+  const int kv_bytes = (int)((uint32_t)n_loc * C::ROWB);
 
   // LDS-direct load roles: lane -> (row in its 1 KiB group, 16-byte slot).
   const int ld_row = lane / C::CHUNKS;

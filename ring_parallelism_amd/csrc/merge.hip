@@ -51,8 +51,10 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p, int row_shift
   float m = -INFINITY, z = 0.f;
   float4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int k = 0; k < p.n_parts; ++k) {
-    const float l = p.lses[k][r];
-    const float4 o = load4<PartT>(p.outs[k], idx);
+    const void* ok = p.strided ? (const void*)((const PartT*)p.outs_base + k * p.out_stride) : p.outs[k];
+    const float* lk = p.strided ? p.lses_base + k * p.lse_stride : p.lses[k];
+    const float l = lk[r];
+    const float4 o = load4<PartT>(ok, idx);
     if (l == -INFINITY) continue;  // no keys in this part (its out is not read)
     if (l > m) {
       const float s = expf(m - l);  // 0 while m = -inf

@@ -87,11 +87,31 @@ struct FwdParams {
 struct MergeParams {
   const void* outs[RA_MAX_PARTS];
   const float* lses[RA_MAX_PARTS];
+  // Strided form (strided != 0): part k at outs_base + k * out_stride elements
+  // and lses_base + k * lse_stride, for any number of parts.
+  const void* outs_base;
+  const float* lses_base;
+  int64_t out_stride, lse_stride;
+  int32_t strided;
   void* out;
   float* lse;
   int64_t n_rows;     // batch * heads * rows
   int32_t head_dim;
   int32_t n_parts;
+};
+
+// Split-KV decode: one query token per (batch, query head) against key ranges
+// of the blocks; one wave per (part, batch, kv head), part = block * n_splits + range.
+struct DecodeParams {
+  const void* q;          // [B, h_q, d] bf16
+  float* out_parts;       // [n_parts, B, h_q, d]
+  float* lse_parts;       // [n_parts, B, h_q]
+  int64_t n_loc;          // keys per block
+  int32_t n_blocks, n_splits, batch, h_q, h_kv, group;
+  int32_t n_items;        // n_blocks * n_splits * batch * h_kv
+  float scale_log2;       // scale * log2(e)
+  const void* k[RA_MAX_BLOCKS];
+  const void* v[RA_MAX_BLOCKS];
 };
 
 // Launchers (defined in the kernel translation units).
@@ -105,6 +125,7 @@ hipError_t launch_merge(const MergeParams& p, int32_t parts_dtype, int32_t out_d
                         hipStream_t stream);
 void tile_shape_f32(int32_t head_dim, int32_t* tq, int32_t* tk);
 void tile_shape_bf16(int32_t head_dim, int32_t* tq, int32_t* tk);
+hipError_t launch_decode_bf16(const DecodeParams& p, int32_t head_dim, hipStream_t stream);
 hipError_t launch_mfma_probe(int64_t iters, float* sink, int32_t n_workgroups, hipStream_t stream);
 constexpr int kProbeThreads = 512;  // eight waves per workgroup
 double mfma_probe_flop(int64_t iters, int32_t n_workgroups);

@@ -187,3 +187,45 @@ def test_mfma_probe_validation():
     expect(ra.EINVAL, ra.ring_attn_mfma_probe, 0, match="iters")
     L = ra.lib()
     assert L.ring_attn_mfma_probe(1, None, None, None, None) == ra.EINVAL
+
+
+def test_decode_validation():
+    kb = [FAKE] * 4
+    d = good_desc()
+    expect(ra.EUNSUPPORTED, ra.ring_attn_decode, good_desc(in_dtype=ra.F32), FAKE, kb, kb, 1, FAKE, FAKE,
+           match="bf16")
+    expect(ra.EUNSUPPORTED, ra.ring_attn_decode, good_desc(out_dtype=ra.BF16), FAKE, kb, kb, 1, FAKE, FAKE,
+           match="fp32")
+    expect(ra.EINVAL, ra.ring_attn_decode, good_desc(flags=ra.FLAG_SYNC_LOADS), FAKE, kb, kb, 1, FAKE, FAKE,
+           match="flags")
+    expect(ra.EUNSUPPORTED, ra.ring_attn_decode, good_desc(h_q=64, h_kv=1), FAKE, kb, kb, 1, FAKE, FAKE,
+           match="32")
+    expect(ra.EINVAL, ra.ring_attn_decode, d, FAKE, [], [], 1, FAKE, FAKE, match="n_blocks")
+    expect(ra.EINVAL, ra.ring_attn_decode, d, FAKE, [FAKE] * 5, [FAKE] * 5, 1, FAKE, FAKE, match="n_blocks")
+    expect(ra.EINVAL, ra.ring_attn_decode, d, FAKE, kb, kb, 0, FAKE, FAKE, match="n_splits")
+    expect(ra.EINVAL, ra.ring_attn_decode, d, FAKE, kb, kb, 257, FAKE, FAKE, match="n_splits")
+    expect(ra.EINVAL, ra.ring_attn_decode, d, None, kb, kb, 1, FAKE, FAKE, match="must be set")
+    expect(ra.EINVAL, ra.ring_attn_decode, d, FAKE + 8, kb, kb, 1, FAKE, FAKE, match="aligned")
+    expect(ra.EINVAL, ra.ring_attn_decode, d, FAKE, [FAKE, None, FAKE, FAKE], kb, 1, FAKE, FAKE, match="NULL")
+
+
+def test_merge_strided_validation():
+    m = ra.ring_attn_merge_strided
+    # batch, heads, rows, head_dim, outs, parts_dtype, lses, out, out_dtype, lse, n_parts, out_stride, lse_stride
+    expect(ra.EINVAL, m, 1, 2, 3, 64, FAKE, ra.F32, FAKE, FAKE * 16, ra.F32, FAKE * 32, 0, 384, 6,
+           match="n_parts")
+    expect(ra.EINVAL, m, 1, 2, 3, 64, FAKE, ra.F32, FAKE, FAKE * 16, ra.F32, FAKE * 32, 2, 383, 6,
+           match="strides")
+    expect(ra.EINVAL, m, 1, 2, 3, 64, FAKE, ra.F32, FAKE, FAKE * 16, ra.F32, FAKE * 32, 2, 384, 5,
+           match="strides")
+    expect(ra.EUNSUPPORTED, m, 1, 2, 3, 96, FAKE, ra.F32, FAKE, FAKE * 16, ra.F32, FAKE * 32, 2, 576, 6,
+           match="head_dim")
+    expect(ra.EINVAL, m, 1, 2, 3, 64, FAKE + 4, ra.F32, FAKE, FAKE * 16, ra.F32, FAKE * 32, 2, 384, 6,
+           match="misaligned")
+    # out inside part 1 (not part 0 exactly)
+    expect(ra.EINVAL, m, 1, 2, 3, 64, FAKE, ra.F32, FAKE * 16, FAKE + 384 * 4, ra.F32, FAKE * 32, 2, 384, 6,
+           match="overlaps")
+    expect(ra.EINVAL, m, 1, 2, 3, 64, FAKE, ra.F32, FAKE * 16, FAKE * 8, ra.F32, FAKE * 16 + 24, 2, 384, 6,
+           match="lse overlaps")
+    expect(ra.EINVAL, m, 1, 2, 3, 64, FAKE, ra.F32, FAKE * 16, FAKE, ra.BF16, FAKE * 32, 2, 384, 6,
+           match="in-place")
