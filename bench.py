@@ -317,6 +317,7 @@ def suite(args):
               "tflops": round(f0 / (st["median_ms"] / 1e3) / 1e12, 1)})
     del qs, ks, vs, scrub
 
+    natural_step_suite(torch, ra, dev, reps)
     decode_suite(torch, ra, dev, reps)
 
     # 262 144 tokens, c = 32, 64/8 heads, shard 0: fused pass, per-block partials
@@ -366,6 +367,52 @@ def suite(args):
           "merge_roofline": {"bound": "hbm", "achieved": round(merge_bytes / (np.median(mm) / 1e3) / 1e9, 1),
                              "peak": 8000.0, "unit": "GB/s",
                              "frac": round(merge_bytes / (np.median(mm) / 1e3) / 1e9 / 8000.0, 4)}})
+
+
+def natural_step_suite(torch, ra, dev, reps):
+    """A whole 131 072-token step in two forms: (a) Q, K, V gathered into shard
+    tensors, then the 16 shard passes; (b) only K, V gathered, each pass reading
+    Q and writing out / lse at global positions (RA_FLAG_NATURAL_QO), so the
+    result lands in natural order with no shard copy of Q or out."""
+    w = workloads.WORKLOAD_BY_NAME["s128k_c16_zigzag_16x1"]
+    c, n = w.n_shards, w.n_loc
+    g = torch.Generator(device=dev).manual_seed(w.seed)
+    mk = lambda h: (torch.randn((w.batch, h, w.seq_len, w.head_dim), generator=g, device=dev)  # noqa: E731
+                    * w.sigma).to(torch.bfloat16)
+    qn, kn, vn = mk(w.h_q), mk(w.h_kv), mk(w.h_kv)
+    esz = 2
+    qs = torch.empty((c, w.batch, w.h_q, n, w.head_dim), dtype=torch.bfloat16, device=dev)
+    ks = torch.empty((c, w.batch, w.h_kv, n, w.head_dim), dtype=torch.bfloat16, device=dev)
+    vs = torch.empty_like(ks)
+    out_s = torch.empty((w.batch, w.h_q, n, w.head_dim), dtype=torch.bfloat16, device=dev)
+    lse_s = torch.empty((w.batch, w.h_q, n), dtype=torch.float32, device=dev)
+    out_n = torch.empty((w.batch, w.h_q, w.seq_len, w.head_dim), dtype=torch.bfloat16, device=dev)
+    lse_n = torch.empty((w.batch, w.h_q, w.seq_len), dtype=torch.float32, device=dev)
+    d_s = ra.make_desc(w.seq_len, c, w.split, w.batch, w.h_q, w.h_kv, w.head_dim, ra.BF16, ra.BF16, True, w.scale)
+    d_n = ra.make_desc(w.seq_len, c, w.split, w.batch, w.h_q, w.h_kv, w.head_dim, ra.BF16, ra.BF16, True, w.scale,
+                       ra.FLAG_NATURAL_QO)
+    own = [[(r - t) % c for t in range(c)] for r in range(c)]
+
+    def kv():
+        ra.zigzag_partition(w.seq_len, c, w.split, None, kn, ks, w.batch * w.h_kv, w.head_dim * esz)
+        ra.zigzag_partition(w.seq_len, c, w.split, None, vn, vs, w.batch * w.h_kv, w.head_dim * esz)
+
+    def step_shard():
+        ra.zigzag_partition(w.seq_len, c, w.split, None, qn, qs, w.batch * w.h_q, w.head_dim * esz)
+        kv()
+        for r in range(c):
+            ra.ring_attn_shard_fwd(d_s, r, qs[r], [ks[j] for j in own[r]], [vs[j] for j in own[r]], out_s, lse_s)
+
+    def step_natural():
+        kv()
+        for r in range(c):
+            ra.ring_attn_shard_fwd(d_n, r, qn, [ks[j] for j in own[r]], [vs[j] for j in own[r]], out_n, lse_n)
+
+    flop = sum(useful_flop(w, shard_pairs(w, r)) for r in range(c))
+    for mode, fn in (("gathered_qkv", step_shard), ("natural_q_out", step_natural)):
+        st = stat(timed(torch, fn, max(1, reps // 2)))
+        emit({"measurement": "whole_step", "workload": w.name, "mode": mode, **st,
+              "tflops": round(flop / (st["median_ms"] / 1e3) / 1e12, 1)})
 
 
 def decode_suite(torch, ra, dev, reps):

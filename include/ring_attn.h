@@ -82,6 +82,16 @@ typedef struct {
  * bf16 inputs only (RA_EUNSUPPORTED with fp32 inputs). */
 #define RA_FLAG_SYNC_LOADS 1u
 
+/* q, out and lse are the natural-order, full-sequence tensors [B, h_q, S, d]
+ * and [B, h_q, S] instead of shard tensors: the call reads the queries of
+ * shard `rank` at their global positions and writes its outputs there, so
+ * the gather of Q and the scatter of out back to natural order happen inside
+ * the kernel and no shard copy of Q or out exists ("Splitting the Sequence",
+ * intro: device k holds chunks k and 2c-1-k; the notes, section 5).  After
+ * the calls for every rank, out and lse hold the whole sequence's result.
+ * K and V blocks stay in shard layout (the blocks that travel the ring). */
+#define RA_FLAG_NATURAL_QO 2u
+
 /* Shard placement and optional gather into shard-major order.
  *
  * perm (device int64[S], may be NULL): perm[r*(S/c) + t] = global position

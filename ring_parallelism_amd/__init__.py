@@ -18,6 +18,7 @@ SPLIT_STRIPED = 2
 F32 = 0
 BF16 = 1
 FLAG_SYNC_LOADS = 1
+FLAG_NATURAL_QO = 2
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 MAX_BLOCKS = 128
 MAX_PARTS = 64

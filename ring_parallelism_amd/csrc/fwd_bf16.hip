@@ -128,7 +128,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
   const int hk = h / p.group;
   const int n_loc = (int)p.n_loc;
   const int64_t kv_off = ((int64_t)b * p.h_kv + hk) * n_loc * D;
-  const int64_t q_off = ((int64_t)b * p.h_q + h) * n_loc;
+  const int64_t q_off = ((int64_t)b * p.h_q + h) * p.qo_rows;  // q / out / lse rows of (b, h)
   // Bytes of one (batch, kv head) slice of a block (< 2^32: n_loc * d < 2^31).
   const int kv_bytes = (int)((uint32_t)n_loc * C::ROWB);
 
@@ -184,7 +184,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       const int row = i0 + (wave * NB + nb) * 32 + lc;
       const bool ok = row < n_loc;
       posq[nb] = ok ? token_pos32(p.rank, row, n_loc, p.c, p.split) : -1;  // -1: past the shard end
-      const __bf16* qp = (const __bf16*)p.q + (q_off + (ok ? row : 0)) * D + g * 8;
+      const int qrow = ok ? (p.qo_natural ? posq[nb] : row) : 0;
+      const __bf16* qp = (const __bf16*)p.q + (q_off + qrow) * D + g * 8;
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) qreg[nb][s] = ok ? *(const bf16x8*)(qp + s * 16) : bf16x8{};
     }
@@ -572,7 +573,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
       const int row = i0 + (wave * NB + nb) * 32 + lc;
       if (row < n_loc) {
-        const int64_t ro = q_off + row;
+        const int64_t ro = q_off + (p.qo_natural ? posq[nb] : row);
         OutT* op = (OutT*)p.out + ro * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)

@@ -40,7 +40,8 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
   const int64_t pos_first = token_pos(p.rank, i0, n_loc, p.c, p.split);
   const int64_t pos_last = token_pos(p.rank, last_row, n_loc, p.c, p.split);
 
-  const float* qp = (const float*)p.q + (((int64_t)b * p.h_q + h) * n_loc + (row_ok ? row : 0)) * D;
+  const int64_t qrow = row_ok ? (p.qo_natural ? pos_q : row) : 0;  // q / out / lse row of this query
+  const float* qp = (const float*)p.q + (((int64_t)b * p.h_q + h) * p.qo_rows + qrow) * D;
   float qv[D], o[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) {
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
   }
 
   if (row_ok) {
-    const int64_t ro = ((int64_t)b * p.h_q + h) * n_loc + row;
+    const int64_t ro = ((int64_t)b * p.h_q + h) * p.qo_rows + qrow;
     float* op = (float*)p.out + ro * D;
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll

@@ -79,6 +79,8 @@ struct FwdParams {
   float scale;         // softmax scale
   float scale_log2;    // scale * log2(e)
   int32_t sync_loads;  // wait for each batch of tile loads right after issuing it
+  int32_t qo_natural;  // q / out / lse rows are global positions of [B, h_q, S, d] tensors
+  int64_t qo_rows;     // rows per (batch, head) of q / out / lse: S/c, or S when qo_natural
   int32_t owner[RA_MAX_BLOCKS];
   const void* k[RA_MAX_BLOCKS];
   const void* v[RA_MAX_BLOCKS];

@@ -80,6 +80,32 @@ def test_shard_fwd_every_row(case):
         assert stats.cpu().tolist() == expected_stats(p, r, tq, tk, causal), f"stats rank {r}"
 
 
+@pytest.mark.parametrize("case", [SMALL_CASES[i] for i in (0, 2, 3, 4, 5, 7, 9, 10, 11)],
+                         ids=lambda c: f"S{c[0]}_c{c[1]}_sp{c[2]}_d{c[6]}_{c[7]}_{'causal' if c[8] else 'full'}")
+def test_natural_qo_matches_shard_layout(case):
+    """Q read and out / lse written at global positions: after every rank has
+    run, the natural-order result is the shard-layout result scattered back,
+    bit for bit, and every row was written."""
+    S, c, split, B, Hq, Hkv, d, dtype, causal = case
+    p = Problem(S, c, split, B, Hq, Hkv, d, dtype, seed=S + c + 1)
+    qn = up(p.q, dtype)
+    out_nat = torch.full((B, Hq, S, d), float("nan"), dtype=torch.float32, device=DEV)
+    lse_nat = torch.full((B, Hq, S), float("nan"), dtype=torch.float32, device=DEV)
+    desc = p.desc(ra.F32, causal, flags=ra.FLAG_NATURAL_QO)
+    n = S // c
+    perm = torch.from_numpy(p.perm).to(DEV)
+    for r in range(c):
+        say(f"natural q/out {case} rank {r}")
+        owners = p.ring_owners(r)
+        ra.ring_attn_shard_fwd(desc, r, qn, [p.ks[j] for j in owners], [p.vs[j] for j in owners], out_nat, lse_nat,
+                               block_owner=owners)
+        o, l, _ = p.run(r, causal=causal)
+        rows = perm[r * n:(r + 1) * n]
+        torch.cuda.synchronize()
+        assert torch.equal(out_nat[:, :, rows], o) and torch.equal(lse_nat[:, :, rows], l), f"rank {r}"
+    assert not torch.isnan(out_nat).any() and not torch.isnan(lse_nat).any()
+
+
 def test_bf16_output_mode():
     p = Problem(2048, 4, ra.SPLIT_ZIGZAG, 1, 4, 1, 128, "bf16", seed=11)
     for r in range(4):
