@@ -7,19 +7,27 @@
 // the end.  Everything stays in fp32 (no reduced-precision products), which
 // is what a 1e-5 absolute bound against fp64 needs.
 //
-// Workgroup = one wavefront = TQ query rows of one (batch, head).  Key/value
+// Workgroup = one wavefront = the query rows of one (batch, head): 64 rows at
+// d = 64, one per lane; 32 rows at d = 128, each split over lanes l and l + 32
+// (64 dimensions each, the two halves of every score added with one lane
+// swap), so that a lane's query and output rows stay in registers.  Key/value
 // tiles of TK rows are staged in LDS and read as broadcasts.  Tiles whose
 // keys all follow the workgroup's last query are skipped without being read.
 #include "ra_common.h"
+#include "tile_common.h"
 
 namespace ra {
 namespace {
 
-constexpr int TQ = 64;
 constexpr int TK = 32;
+constexpr int kHalf = 64;  // dimensions held per lane
+template <int D>
+constexpr int rows_per_wave() { return 64 / (D / kHalf); }
 
 template <int D>
 __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
+  constexpr int SPLIT = D / kHalf;  // lanes per query row
+  constexpr int TQ = rows_per_wave<D>();
   __shared__ float ks[TK][D];
   __shared__ float vs[TK][D];
 
@@ -31,8 +39,10 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
   const int hk = h / p.group;
   const int64_t n_loc = p.n_loc;
 
+  const int part = lane / TQ;  // which 64 dimensions of the row this lane holds
+  const int d0 = part * kHalf;
   const int64_t i0 = (int64_t)qt * TQ;
-  const int64_t row = i0 + lane;
+  const int64_t row = i0 + lane % TQ;
   const bool row_ok = row < n_loc;
   const int64_t last_row = (i0 + TQ <= n_loc ? i0 + TQ : n_loc) - 1;
   const bool rows_full = i0 + TQ <= n_loc;
@@ -42,10 +52,10 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
 
   const int64_t qrow = row_ok ? (p.qo_natural ? pos_q : row) : 0;  // q / out / lse row of this query
   const float* qp = (const float*)p.q + (((int64_t)b * p.h_q + h) * p.qo_rows + qrow) * D;
-  float qv[D], o[D];
+  float qv[kHalf], o[kHalf];
 #pragma unroll
-  for (int e = 0; e < D; ++e) {
-    qv[e] = row_ok ? qp[e] : 0.f;
+  for (int e = 0; e < kHalf; ++e) {
+    qv[e] = row_ok ? qp[d0 + e] : 0.f;
     o[e] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
@@ -82,30 +92,31 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
       for (int kk = 0; kk < TK; ++kk) {
         float dot = 0.f;
 #pragma unroll
-        for (int e = 0; e < D; ++e) dot = fmaf(qv[e], ks[kk][e], dot);
+        for (int e = 0; e < kHalf; ++e) dot = fmaf(qv[e], ks[kk][d0 + e], dot);
+        if constexpr (SPLIT == 2) dot = halves_sum(dot);  // both halves hold the full score
         bool vis = true;
         if (masked) {
           const int64_t jj = key0 + kk;
           vis = row_ok && jj < n_loc &&
                 (!p.causal || token_pos(j, jj, n_loc, p.c, p.split) <= pos_q);
-          pairs += vis ? 1 : 0;
+          pairs += (vis && part == 0) ? 1 : 0;
         }
         s[kk] = vis ? dot * p.scale : -INFINITY;
         mt = fmaxf(mt, s[kk]);
       }
-      if (!masked) pairs += TK;
+      if (!masked && part == 0) pairs += TK;
       const float m_new = fmaxf(m, mt);
       if (m_new == -INFINITY) continue;  // nothing visible to this row yet
       const float alpha = expf(m - m_new);  // m = -inf gives 0
       l *= alpha;
 #pragma unroll
-      for (int e = 0; e < D; ++e) o[e] *= alpha;
+      for (int e = 0; e < kHalf; ++e) o[e] *= alpha;
 #pragma unroll 4
       for (int kk = 0; kk < TK; ++kk) {
         const float pk = expf(s[kk] - m_new);
         l += pk;
 #pragma unroll
-        for (int e = 0; e < D; ++e) o[e] = fmaf(pk, vs[kk][e], o[e]);
+        for (int e = 0; e < kHalf; ++e) o[e] = fmaf(pk, vs[kk][d0 + e], o[e]);
       }
       m = m_new;
     }
@@ -116,8 +127,8 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
     float* op = (float*)p.out + ro * D;
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-    for (int e = 0; e < D; ++e) op[e] = o[e] * inv;
-    p.lse[ro] = l > 0.f ? m + logf(l) : -INFINITY;
+    for (int e = 0; e < kHalf; ++e) op[d0 + e] = o[e] * inv;
+    if (part == 0) p.lse[ro] = l > 0.f ? m + logf(l) : -INFINITY;
   }
 
   if (p.stats) {
@@ -135,13 +146,13 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
 }  // namespace
 
 void tile_shape_f32(int32_t head_dim, int32_t* tq, int32_t* tk) {
-  (void)head_dim;
-  *tq = TQ;
+  *tq = head_dim == 64 ? rows_per_wave<64>() : rows_per_wave<128>();
   *tk = TK;
 }
 
 hipError_t launch_fwd_f32(const FwdParams& p0, int32_t head_dim, hipStream_t stream) {
   FwdParams p = p0;
+  const int TQ = head_dim == 64 ? rows_per_wave<64>() : rows_per_wave<128>();
   p.n_qtiles = (int32_t)((p.n_loc + TQ - 1) / TQ);
   p.n_ktiles = (int32_t)((p.n_loc + TK - 1) / TK);
   p.n_pairs = p.n_qtiles;
