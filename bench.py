@@ -174,6 +174,8 @@ def main():
     sink = torch.empty(nwg * 512, dtype=torch.float32, device=dev)
     probe_ms = timed(torch, lambda: ra.ring_attn_mfma_probe(2000, sink), 3)
     probe_tf = pflop / (float(np.median(probe_ms)) / 1e3) / 1e12
+    probe_rnd_ms = timed(torch, lambda: ra.ring_attn_mfma_probe(2000, sink, random_operands=True), 3)
+    probe_rnd_tf = pflop / (float(np.median(probe_rnd_ms)) / 1e3) / 1e12
 
     pairs = [shard_pairs(w, r) for r in range(c)]               # per query head
     flop_step = sum(useful_flop(w, pr) for pr in pairs)
@@ -203,7 +205,9 @@ def main():
                      "flop_per_launch": flop_launch, "avg_launch_ms": round(avg_kernel_s * 1e3, 4),
                      "launches_timed": len(kernel_ms),
                      "probe_sustained_tflops": round(probe_tf, 1),
-                     "frac_of_probe": round(achieved / probe_tf, 4)},
+                     "frac_of_probe": round(achieved / probe_tf, 4),
+                     "probe_random_operands_tflops": round(probe_rnd_tf, 1),
+                     "frac_of_probe_random": round(achieved / probe_rnd_tf, 4)},
         "stats_per_step": {"pairs": int(pairs_counted), "tiles_full": st[1] // args.steps,
                            "tiles_partial": st[2] // args.steps, "tiles_skipped": st[3] // args.steps},
     }
@@ -263,11 +267,13 @@ def suite(args):
     # Sustained bf16 MFMA rate of this device with the attention step's matrix mix.
     nwg, flop = ra.ring_attn_mfma_probe(2000)
     sink = torch.empty(nwg * 512, dtype=torch.float32, device=dev)
-    ms = timed(torch, lambda: ra.ring_attn_mfma_probe(2000, sink), reps)
-    tf = flop / (np.median(ms) / 1e3) / 1e12
-    emit({"measurement": "mfma_probe", "workgroups": nwg, "flop": flop, **stat(ms),
-          "tflops": round(tf, 1), "pct_of_nominal": round(100 * tf / PEAK_BF16_TFLOPS, 2),
-          "implied_clock_ghz_at_4096_flop_per_clk_per_cu": round(tf * 1e12 / (nwg * 4096) / 1e9, 3)})
+    for rnd in (False, True):
+        ms = timed(torch, lambda: ra.ring_attn_mfma_probe(2000, sink, random_operands=rnd), reps)
+        tf = flop / (np.median(ms) / 1e3) / 1e12
+        emit({"measurement": "mfma_probe", "operands": "random N(0,1) bf16" if rnd else "fixed low-entropy",
+              "workgroups": nwg, "flop": flop, **stat(ms),
+              "tflops": round(tf, 1), "pct_of_nominal": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+              "implied_clock_ghz_at_4096_flop_per_clk_per_cu": round(tf * 1e12 / (nwg * 4096) / 1e9, 3)})
 
     def fwd(w, desc, r, q, ks, vs, out, lse, owners=None):
         c = w.n_shards

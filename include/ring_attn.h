@@ -223,6 +223,9 @@ int32_t ring_attn_abi_version(void);
  * four chains of two, no memory traffic) run `iters` times by eight waves on
  * every compute unit, so that the sustained bf16 MFMA rate (and hence the
  * shader clock under matrix load) can be timed next to the attention kernel.
+ * The rate depends on the operand values through the chip's power limit:
+ * operands = 0 uses fixed low-entropy fragments, operands = 1 pseudo-random
+ * N(0,1)-like bf16 values (the attention workloads' distribution).
  * Not part of the attention path.
  *
  * iters >= 1; sink (device float[*n_workgroups * 512], caller-owned) receives
@@ -230,8 +233,8 @@ int32_t ring_attn_abi_version(void);
  * *n_workgroups is the number of workgroups launched (the device's compute
  * unit count) and *flop the dense FLOP the launch performs.  Passing sink =
  * NULL only fills *n_workgroups and *flop (nothing is launched). */
-ra_status ring_attn_mfma_probe(int64_t iters, float* sink, int32_t* n_workgroups, double* flop,
-                               void* stream);
+ra_status ring_attn_mfma_probe(int64_t iters, int32_t operands, float* sink, int32_t* n_workgroups,
+                               double* flop, void* stream);
 
 #ifdef __cplusplus
 }

@@ -73,7 +73,7 @@ def lib():
     L.ring_attn_shard_fwd.argtypes = [ctypes.POINTER(AttnDesc), i32, vp, i32, vp, vp, vp, vp, vp, vp, vp]
     L.ring_attn_tile_shape.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.ring_attn_merge.argtypes = [i32, i32, i64, i32, i32, vp, i32, vp, vp, i32, vp, vp]
-    L.ring_attn_mfma_probe.argtypes = [i64, vp, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double), vp]
+    L.ring_attn_mfma_probe.argtypes = [i64, i32, vp, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double), vp]
     L.ring_attn_merge_strided.argtypes = [i32, i32, i64, i32, i32, vp, i64, i32, vp, i64, vp, i32, vp, vp]
     L.ring_attn_decode.argtypes = [ctypes.POINTER(AttnDesc), vp, i32, vp, vp, i32, vp, vp, vp]
     for name in ("zigzag_partition", "zigzag_unpartition", "ring_attn_shard_fwd",
@@ -196,13 +196,13 @@ def ring_attn_decode(desc, q, k_blocks, v_blocks, n_splits, out_parts, lse_parts
                                   _ptr(lse_parts), _stream(stream, q, out_parts)))
 
 
-def ring_attn_mfma_probe(iters, sink=None, stream=None):
+def ring_attn_mfma_probe(iters, sink=None, random_operands=False, stream=None):
     """Launch the matrix-core calibration probe (``sink``: device float32 tensor
     of at least n_workgroups * 512 elements; None only queries).  Returns
     ``(n_workgroups, flop)`` of the launch."""
     nwg, flop = ctypes.c_int32(0), ctypes.c_double(0.0)
-    _check(lib().ring_attn_mfma_probe(int(iters), _ptr(sink), ctypes.byref(nwg), ctypes.byref(flop),
-                                      _stream(stream, sink)))
+    _check(lib().ring_attn_mfma_probe(int(iters), int(bool(random_operands)), _ptr(sink), ctypes.byref(nwg),
+                                      ctypes.byref(flop), _stream(stream, sink)))
     return int(nwg.value), float(flop.value)
 
 

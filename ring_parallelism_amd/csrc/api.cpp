@@ -236,9 +236,10 @@ ra_status ring_attn_merge(int32_t batch, int32_t heads, int64_t rows, int32_t he
 }
 
 
-ra_status ring_attn_mfma_probe(int64_t iters, float* sink, int32_t* n_workgroups, double* flop,
-                               void* stream) {
+ra_status ring_attn_mfma_probe(int64_t iters, int32_t operands, float* sink, int32_t* n_workgroups,
+                               double* flop, void* stream) {
   if (iters < 1) return fail(RA_EINVAL, "iters must be >= 1");
+  if (operands != 0 && operands != 1) return fail(RA_EINVAL, "operands must be 0 (fixed) or 1 (random)");
   if (!n_workgroups || !flop) return fail(RA_EINVAL, "n_workgroups and flop must be set");
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -249,7 +250,7 @@ ra_status ring_attn_mfma_probe(int64_t iters, float* sink, int32_t* n_workgroups
   *flop = ra::mfma_probe_flop(iters, cus);
   if (!sink) return ok();
   if (!aligned(sink, 4)) return fail(RA_EINVAL, "sink must be 4-byte aligned");
-  e = ra::launch_mfma_probe(iters, sink, cus, (hipStream_t)stream);
+  e = ra::launch_mfma_probe(iters, operands, sink, cus, (hipStream_t)stream);
   if (e != hipSuccess) return fail(RA_EHIP, "probe launch failed: %s", hipGetErrorString(e));
   return ok();
 }

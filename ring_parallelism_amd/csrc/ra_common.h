@@ -128,7 +128,7 @@ hipError_t launch_merge(const MergeParams& p, int32_t parts_dtype, int32_t out_d
 void tile_shape_f32(int32_t head_dim, int32_t* tq, int32_t* tk);
 void tile_shape_bf16(int32_t head_dim, int32_t* tq, int32_t* tk);
 hipError_t launch_decode_bf16(const DecodeParams& p, int32_t head_dim, hipStream_t stream);
-hipError_t launch_mfma_probe(int64_t iters, float* sink, int32_t n_workgroups, hipStream_t stream);
+hipError_t launch_mfma_probe(int64_t iters, int32_t mode, float* sink, int32_t n_workgroups, hipStream_t stream);
 constexpr int kProbeThreads = 512;  // eight waves per workgroup
 double mfma_probe_flop(int64_t iters, int32_t n_workgroups);
 

@@ -187,7 +187,8 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
 def test_mfma_probe_validation():
     expect(ra.EINVAL, ra.ring_attn_mfma_probe, 0, match="iters")
     L = ra.lib()
-    assert L.ring_attn_mfma_probe(1, None, None, None, None) == ra.EINVAL
+    assert L.ring_attn_mfma_probe(1, 0, None, None, None, None) == ra.EINVAL
+    assert L.ring_attn_mfma_probe(1, 2, None, None, None, None) == ra.EINVAL
 
 
 def test_decode_validation():

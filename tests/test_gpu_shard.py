@@ -139,9 +139,11 @@ def test_mfma_probe_runs():
     assert nwg >= 1 and flop == 2.0 * 32 * 32 * 16 * 16 * 4 * 8 * nwg
     sink = torch.full((nwg * 512,), float("nan"), dtype=torch.float32, device=DEV)
     say("mfma probe")
-    assert ra.ring_attn_mfma_probe(4, sink) == (nwg, flop)
-    torch.cuda.synchronize()
-    assert torch.isfinite(sink).all()
+    for rnd in (False, True):
+        sink.fill_(float("nan"))
+        assert ra.ring_attn_mfma_probe(4, sink, random_operands=rnd) == (nwg, flop)
+        torch.cuda.synchronize()
+        assert torch.isfinite(sink).all()
 
 
 # ---------------------------------------------------------------- partial results and merge
