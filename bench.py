@@ -323,6 +323,7 @@ def suite(args):
               "tflops": round(f0 / (st["median_ms"] / 1e3) / 1e12, 1)})
     del qs, ks, vs, scrub
 
+    split_suite(torch, ra, dev, reps)
     natural_step_suite(torch, ra, dev, reps)
     decode_suite(torch, ra, dev, reps)
 
@@ -373,6 +374,38 @@ def suite(args):
           "merge_roofline": {"bound": "hbm", "achieved": round(merge_bytes / (np.median(mm) / 1e3) / 1e9, 1),
                              "peak": 8000.0, "unit": "GB/s",
                              "frac": round(merge_bytes / (np.median(mm) / 1e3) / 1e9 / 8000.0, 4)}})
+
+
+def split_suite(torch, ra, dev, reps):
+    """Small shards (8 192 tokens / c = 8 with 32/8 heads; 32 768 / c = 16 with
+    16/1 heads) leave most compute units idle in one pass (64 workgroups);
+    ring_attn_shard_fwd_split runs groups of blocks concurrently and merges."""
+    for name in ("s8k_c8_zigzag_gqa32x8", "s32k_c16_zigzag_16x1"):
+        w = workloads.WORKLOAD_BY_NAME[name]
+        qs, ks, vs = device_inputs(w, torch, dev, blocks_for=[0])
+        c, n = w.n_shards, w.n_loc
+        out = torch.empty((w.batch, w.h_q, n, w.head_dim), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((w.batch, w.h_q, n), dtype=torch.float32, device=dev)
+        desc = ra.make_desc(w.seq_len, c, w.split, w.batch, w.h_q, w.h_kv, w.head_dim, ra.BF16, ra.BF16, True,
+                            w.scale)
+        own = [(0 - t) % c for t in range(c)]
+        kb, vb = [ks[j] for j in own], [vs[j] for j in own]
+        fl = useful_flop(w, shard_pairs(w, 0))
+        res = {}
+        for ns in (1, 2, 4, 8):
+            if ns > c:
+                continue
+            if ns == 1:
+                fn = lambda: ra.ring_attn_shard_fwd(desc, 0, qs[0], kb, vb, out, lse, block_owner=own)  # noqa: E731
+            else:
+                work = torch.empty((ns, w.batch, w.h_q, n, w.head_dim), dtype=torch.float32, device=dev)
+                work_l = torch.empty((ns, w.batch, w.h_q, n), dtype=torch.float32, device=dev)
+                fn = lambda: ra.ring_attn_shard_fwd_split(desc, 0, qs[0], kb, vb, ns, work, work_l, out,  # noqa: E731
+                                                          lse, block_owner=own)
+            st = stat(timed(torch, fn, reps))
+            res[str(ns)] = {**st, "tflops": round(fl / (st["median_ms"] / 1e3) / 1e12, 1)}
+        emit({"measurement": "small_shard_split", "workload": w.name, "rank": 0, "by_n_splits": res})
+        del qs, ks, vs
 
 
 def natural_step_suite(torch, ra, dev, reps):

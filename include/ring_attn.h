@@ -177,6 +177,23 @@ ra_status ring_attn_merge(int32_t batch, int32_t heads, int64_t rows, int32_t he
                           const float* const* lses, void* out, int32_t out_dtype, float* lse,
                           void* stream);
 
+/* ring_attn_shard_fwd for shards too small to fill the device: the block
+ * list is cut into n_splits groups of consecutive blocks (1 <= n_splits <=
+ * n_blocks), the groups run concurrently, each writing a partial result
+ * (the online-softmax fold over its blocks, "Sequence / context parallelism"
+ * notes, section 4) to the caller's workspace, and the partials are folded
+ * into out / lse by the merge of ring_attn_merge.  The result equals
+ * ring_attn_shard_fwd's up to rounding; stats count the same tiles.
+ *
+ * work_out: device fp32 [n_splits, B, h_q, S/c, d]; work_lse: device fp32
+ * [n_splits, B, h_q, S/c]; both caller-owned scratch, overwritten, and must
+ * not overlap out / lse.  bf16 inputs only, no RA_FLAG_NATURAL_QO
+ * (RA_EUNSUPPORTED).  Other arguments and errors as ring_attn_shard_fwd. */
+ra_status ring_attn_shard_fwd_split(const ra_attn_desc* desc, int32_t rank, const void* q, int32_t n_blocks,
+                                    const int32_t* block_owner, const void* const* k_blocks,
+                                    const void* const* v_blocks, int32_t n_splits, float* work_out,
+                                    float* work_lse, void* out, float* lse, int64_t* stats, void* stream);
+
 /* ring_attn_merge with the parts in one buffer: part k's out starts
  * out_stride elements after part k-1's (parts_dtype elements, out_stride >=
  * batch*heads*rows*head_dim) and its lse lse_stride values after part k-1's

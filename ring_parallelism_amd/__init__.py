@@ -29,7 +29,7 @@ LIB_PATH = os.environ.get("RING_ATTN_LIB") or os.path.join(os.path.dirname(os.pa
 
 EXPORTS = ("zigzag_partition", "zigzag_unpartition", "ring_attn_shard_fwd", "ring_attn_tile_shape",
            "ring_attn_merge", "ring_attn_last_error", "ring_attn_abi_version", "ring_attn_mfma_probe",
-           "ring_attn_merge_strided", "ring_attn_decode")
+           "ring_attn_merge_strided", "ring_attn_decode", "ring_attn_shard_fwd_split")
 
 
 class RingAttnError(RuntimeError):
@@ -76,9 +76,11 @@ def lib():
     L.ring_attn_mfma_probe.argtypes = [i64, i32, vp, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double), vp]
     L.ring_attn_merge_strided.argtypes = [i32, i32, i64, i32, i32, vp, i64, i32, vp, i64, vp, i32, vp, vp]
     L.ring_attn_decode.argtypes = [ctypes.POINTER(AttnDesc), vp, i32, vp, vp, i32, vp, vp, vp]
+    L.ring_attn_shard_fwd_split.argtypes = [ctypes.POINTER(AttnDesc), i32, vp, i32, vp, vp, vp, i32, vp, vp, vp,
+                                            vp, vp, vp]
     for name in ("zigzag_partition", "zigzag_unpartition", "ring_attn_shard_fwd",
                  "ring_attn_tile_shape", "ring_attn_merge", "ring_attn_mfma_probe",
-                 "ring_attn_merge_strided", "ring_attn_decode"):
+                 "ring_attn_merge_strided", "ring_attn_decode", "ring_attn_shard_fwd_split"):
         getattr(L, name).restype = i32
     L.ring_attn_last_error.restype = ctypes.c_char_p
     L.ring_attn_abi_version.restype = i32
@@ -158,6 +160,26 @@ def ring_attn_shard_fwd(desc: AttnDesc, rank, q, k_blocks, v_blocks, out, lse, b
         owners = (ctypes.c_int32 * n)(*[int(x) for x in block_owner])
     _check(lib().ring_attn_shard_fwd(ctypes.byref(desc), int(rank), _ptr(q), n, owners, kp, vp,
                                      _ptr(out), _ptr(lse), _ptr(stats), _stream(stream, q, out)))
+
+
+def ring_attn_shard_fwd_split(desc, rank, q, k_blocks, v_blocks, n_splits, work_out, work_lse, out, lse,
+                              block_owner=None, stats=None, stream=None):
+    """ring_attn_shard_fwd with the block list cut into ``n_splits`` concurrent
+    groups (partials in the fp32 workspace ``work_out`` [n_splits, B, h_q, S/c, d]
+    and ``work_lse`` [n_splits, B, h_q, S/c]), folded into ``out`` / ``lse``."""
+    n = len(k_blocks)
+    if len(v_blocks) != n:
+        raise ValueError("k_blocks and v_blocks differ in length")
+    kp = (ctypes.c_void_p * max(n, 1))(*[_ptr(t) for t in k_blocks])
+    vp = (ctypes.c_void_p * max(n, 1))(*[_ptr(t) for t in v_blocks])
+    owners = None
+    if block_owner is not None:
+        if len(block_owner) != n:
+            raise ValueError("block_owner and k_blocks differ in length")
+        owners = (ctypes.c_int32 * n)(*[int(x) for x in block_owner])
+    _check(lib().ring_attn_shard_fwd_split(ctypes.byref(desc), int(rank), _ptr(q), n, owners, kp, vp, int(n_splits),
+                                           _ptr(work_out), _ptr(work_lse), _ptr(out), _ptr(lse), _ptr(stats),
+                                           _stream(stream, q, out)))
 
 
 def ring_attn_merge(batch, heads, rows, head_dim, outs, parts_dtype, lses, out, out_dtype, lse,

@@ -133,10 +133,11 @@ ra_status ring_attn_tile_shape(const ra_attn_desc* desc, int32_t* tile_q, int32_
   return ok();
 }
 
-ra_status ring_attn_shard_fwd(const ra_attn_desc* desc, int32_t rank, const void* q,
-                              int32_t n_blocks, const int32_t* block_owner,
-                              const void* const* k_blocks, const void* const* v_blocks, void* out,
-                              float* lse, int64_t* stats, void* stream) {
+// Validates the arguments shared by the two shard entry points and fills p.
+static ra_status shard_params(const ra_attn_desc* desc, int32_t rank, const void* q, int32_t n_blocks,
+                              const int32_t* block_owner, const void* const* k_blocks,
+                              const void* const* v_blocks, void* out, float* lse, int64_t* stats,
+                              ra::FwdParams& p) {
   ra_status st = check_desc(desc);
   if (st != RA_OK) return st;
   const int32_t c = desc->n_shards;
@@ -151,7 +152,6 @@ ra_status ring_attn_shard_fwd(const ra_attn_desc* desc, int32_t rank, const void
   if (stats && !aligned(stats, 8)) return fail(RA_EINVAL, "stats must be 8-byte aligned");
   if (!k_blocks || !v_blocks) return fail(RA_EINVAL, "k_blocks and v_blocks must be set");
 
-  ra::FwdParams p;
   std::memset(&p, 0, sizeof p);
   for (int t = 0; t < n_blocks; ++t) {
     const int32_t j = block_owner ? block_owner[t] : (int32_t)(((int64_t)rank - t % c + c) % c);
@@ -185,11 +185,71 @@ ra_status ring_attn_shard_fwd(const ra_attn_desc* desc, int32_t rank, const void
   p.sync_loads = (desc->flags & RA_FLAG_SYNC_LOADS) ? 1 : 0;
   p.qo_natural = (desc->flags & RA_FLAG_NATURAL_QO) ? 1 : 0;
   p.qo_rows = p.qo_natural ? desc->seq_len : p.n_loc;
+  p.n_splits = 1;
+  return RA_OK;
+}
 
+ra_status ring_attn_shard_fwd(const ra_attn_desc* desc, int32_t rank, const void* q,
+                              int32_t n_blocks, const int32_t* block_owner,
+                              const void* const* k_blocks, const void* const* v_blocks, void* out,
+                              float* lse, int64_t* stats, void* stream) {
+  ra::FwdParams p;
+  ra_status st = shard_params(desc, rank, q, n_blocks, block_owner, k_blocks, v_blocks, out, lse, stats, p);
+  if (st != RA_OK) return st;
   hipError_t e = desc->in_dtype == RA_F32
                      ? ra::launch_fwd_f32(p, desc->head_dim, (hipStream_t)stream)
                      : ra::launch_fwd_bf16(p, desc->head_dim, desc->out_dtype, (hipStream_t)stream);
   if (e != hipSuccess) return fail(RA_EHIP, "shard_fwd launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+ra_status ring_attn_shard_fwd_split(const ra_attn_desc* desc, int32_t rank, const void* q, int32_t n_blocks,
+                                    const int32_t* block_owner, const void* const* k_blocks,
+                                    const void* const* v_blocks, int32_t n_splits, float* work_out,
+                                    float* work_lse, void* out, float* lse, int64_t* stats, void* stream) {
+  if (desc && desc->in_dtype != RA_BF16)
+    return fail(RA_EUNSUPPORTED, "the split pass takes bf16 inputs");
+  if (desc && (desc->flags & RA_FLAG_NATURAL_QO))
+    return fail(RA_EUNSUPPORTED, "the split pass writes shard-layout results (no RA_FLAG_NATURAL_QO)");
+  ra::FwdParams p;
+  ra_status st = shard_params(desc, rank, q, n_blocks, block_owner, k_blocks, v_blocks, out, lse, stats, p);
+  if (st != RA_OK) return st;
+  if (n_splits < 1 || n_splits > n_blocks)
+    return fail(RA_EINVAL, "n_splits %d not in [1, n_blocks=%d]", n_splits, n_blocks);
+  if (!work_out || !work_lse) return fail(RA_EINVAL, "work_out and work_lse must be set");
+  if (!aligned(work_out, 16) || !aligned(work_lse, 4))
+    return fail(RA_EINVAL, "work_out must be 16-byte aligned, work_lse 4-byte");
+  const int64_t rows = (int64_t)desc->batch * desc->h_q * p.n_loc;
+  const int64_t part = rows * desc->head_dim;
+  // The workspace must not overlap the result.
+  const char* w0 = (const char*)work_out;
+  const char* w1 = w0 + n_splits * part * 4;
+  const char* o0 = (const char*)out;
+  const char* o1 = o0 + part * (desc->out_dtype == RA_F32 ? 4 : 2);
+  if (o0 < w1 && o1 > w0) return fail(RA_EINVAL, "out overlaps work_out");
+  if ((const char*)lse < (const char*)(work_lse + n_splits * rows) && (const char*)(lse + rows) > (const char*)work_lse)
+    return fail(RA_EINVAL, "lse overlaps work_lse");
+  p.out = work_out;
+  p.lse = work_lse;
+  p.n_splits = n_splits;
+  p.part_stride_out = part;
+  p.part_stride_lse = rows;
+  hipError_t e = ra::launch_fwd_bf16(p, desc->head_dim, RA_F32, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RA_EHIP, "split shard pass launch failed: %s", hipGetErrorString(e));
+  ra::MergeParams m;
+  std::memset(&m, 0, sizeof m);
+  m.strided = 1;
+  m.outs_base = work_out;
+  m.lses_base = work_lse;
+  m.out_stride = part;
+  m.lse_stride = rows;
+  m.out = out;
+  m.lse = lse;
+  m.n_rows = rows;
+  m.head_dim = desc->head_dim;
+  m.n_parts = n_splits;
+  e = ra::launch_merge(m, RA_F32, desc->out_dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RA_EHIP, "merge launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -121,7 +121,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
   // items on one XCD.
   const int G = gridDim.x;
   const int bid = blockIdx.x;
-  const int wl = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  const int wl_all = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  // Split of the block list (one group when n_splits = 1): this workgroup
+  // folds blocks [t0, t1) and writes its own partial result.
+  const int split = wl_all / p.grid_per_split;
+  const int wl = wl_all % p.grid_per_split;
+  const int t0 = split * p.n_blocks / p.n_splits, t1 = (split + 1) * p.n_blocks / p.n_splits;
+  OutT* const out_base = (OutT*)p.out + split * p.part_stride_out;
+  float* const lse_base = p.lse + split * p.part_stride_lse;
   const int h = wl % p.h_q;
   const int pair = (wl / p.h_q) % p.n_pairs;
   const int b = wl / (p.h_q * p.n_pairs);
@@ -222,16 +229,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       x.full = rows_full ? c_first / kBK : 0;
     };
     auto advance = [&](Tile x) {
-      if (x.t >= p.n_blocks) return x;
+      if (x.t >= t1) return x;
       if (++x.kt < x.vis) return x;
       x.kt = 0;
-      while (++x.t < p.n_blocks) {
+      while (++x.t < t1) {
         block_counts(x);
         if (x.vis > 0) break;
       }
       return x;
     };
-    auto valid = [&](const Tile& x) { return x.t < p.n_blocks; };
+    auto valid = [&](const Tile& x) { return x.t < t1; };
 
     // Put tile x's K and V into LDS stage `st`.  Rows past the shard end fall
     // outside the buffer resource and read as zeros.
@@ -444,7 +451,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
     first.full = 0;
     first.kb = first.vb = nullptr;
     int n_tiles = 0;
-    for (int t = 0; t < p.n_blocks; ++t) {
+    for (int t = t0; t < t1; ++t) {
       Tile x;
       x.t = t;
       block_counts(x);
@@ -574,7 +581,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       const int row = i0 + (wave * NB + nb) * 32 + lc;
       if (row < n_loc) {
         const int64_t ro = q_off + (p.qo_natural ? posq[nb] : row);
-        OutT* op = (OutT*)p.out + ro * D;
+        OutT* op = out_base + ro * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -596,7 +603,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
               *(bf16x4*)(op + d0) = v4;
             }
           }
-        if (g == 0) p.lse[ro] = lt > 0.f ? (m_ref[nb] + __log2f(lt)) * kLn2 : -INFINITY;
+        if (g == 0) lse_base[ro] = lt > 0.f ? (m_ref[nb] + __log2f(lt)) * kLn2 : -INFINITY;
       }
     }
   }
@@ -612,7 +619,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       const int last_row = (rows_full ? i0 + C::BQ : n_loc) - 1;
       const int pos_first = token_pos32(p.rank, i0, n_loc, p.c, p.split);
       const int pos_last = token_pos32(p.rank, last_row, n_loc, p.c, p.split);
-      for (int t = 0; t < p.n_blocks; ++t) {
+      for (int t = t0; t < t1; ++t) {
         const int j = p.owner[t];
         const int c_last = p.causal ? count_upto32(j, pos_last, n_loc, p.c, p.split) : n_loc;
         const int c_first = p.causal ? count_upto32(j, pos_first, n_loc, p.c, p.split) : n_loc;
@@ -654,8 +661,10 @@ hipError_t launch_one(FwdParams p, hipStream_t stream) {
   p.n_qtiles = (int32_t)((p.n_loc + C::BQ - 1) / C::BQ);
   p.n_ktiles = (int32_t)((p.n_loc + C::BK - 1) / C::BK);
   p.n_pairs = (p.n_qtiles + 1) / 2;
-  const int64_t grid = (int64_t)p.batch * p.h_q * p.n_pairs;
+  const int64_t per_split = (int64_t)p.batch * p.h_q * p.n_pairs;
+  const int64_t grid = per_split * p.n_splits;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  p.grid_per_split = (int32_t)per_split;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, T::NW, T::NB, T::MB, OutT>), dim3((unsigned)grid),
                      dim3(C::NT), 0, stream, p);
   return hipGetLastError();

@@ -81,6 +81,10 @@ struct FwdParams {
   int32_t sync_loads;  // wait for each batch of tile loads right after issuing it
   int32_t qo_natural;  // q / out / lse rows are global positions of [B, h_q, S, d] tensors
   int64_t qo_rows;     // rows per (batch, head) of q / out / lse: S/c, or S when qo_natural
+  // Split over the block list: n_splits groups of consecutive blocks, each
+  // written as a partial to out / lse + split * part_stride (1: no split).
+  int32_t n_splits, grid_per_split;
+  int64_t part_stride_out, part_stride_lse;
   int32_t owner[RA_MAX_BLOCKS];
   const void* k[RA_MAX_BLOCKS];
   const void* v[RA_MAX_BLOCKS];

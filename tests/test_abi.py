@@ -231,3 +231,19 @@ def test_merge_strided_validation():
            match="lse overlaps")
     expect(ra.EINVAL, m, 1, 2, 3, 64, FAKE, ra.F32, FAKE * 16, FAKE, ra.BF16, FAKE * 32, 2, 384, 6,
            match="in-place")
+
+
+def test_shard_fwd_split_validation():
+    kb = [FAKE] * 4
+    f = ra.ring_attn_shard_fwd_split
+    W = FAKE * 64
+    expect(ra.EUNSUPPORTED, f, good_desc(in_dtype=ra.F32, head_dim=64), 0, FAKE, kb, kb, 2, W, W, FAKE, FAKE,
+           match="bf16")
+    expect(ra.EUNSUPPORTED, f, good_desc(flags=ra.FLAG_NATURAL_QO), 0, FAKE, kb, kb, 2, W, W, FAKE, FAKE,
+           match="NATURAL")
+    expect(ra.EINVAL, f, good_desc(), 0, FAKE, kb, kb, 0, W, W, FAKE, FAKE, match="n_splits")
+    expect(ra.EINVAL, f, good_desc(), 0, FAKE, kb, kb, 5, W, W, FAKE, FAKE, match="n_splits")
+    expect(ra.EINVAL, f, good_desc(), 0, FAKE, kb, kb, 2, None, W, FAKE, FAKE, match="work")
+    expect(ra.EINVAL, f, good_desc(), 0, FAKE, kb, kb, 2, W + 8, W, FAKE, FAKE, match="aligned")
+    expect(ra.EINVAL, f, good_desc(), 0, FAKE, kb, kb, 2, W, W * 2, W + 16, FAKE, match="overlaps")
+    expect(ra.EINVAL, f, good_desc(), 9, FAKE, kb, kb, 2, W, W, FAKE, FAKE, match="rank")

@@ -106,6 +106,37 @@ def test_natural_qo_matches_shard_layout(case):
     assert not torch.isnan(out_nat).any() and not torch.isnan(lse_nat).any()
 
 
+@pytest.mark.parametrize("S,c,split,B,Hq,Hkv,d,n_splits,out_dtype", [
+    (4096, 4, ra.SPLIT_ZIGZAG, 1, 4, 1, 128, 2, ra.F32),
+    (4096, 8, ra.SPLIT_CONTIGUOUS, 1, 4, 2, 128, 8, ra.F32),   # one block per group
+    (1040, 4, ra.SPLIT_ZIGZAG, 2, 4, 2, 128, 3, ra.F32),        # ragged tiles, uneven groups
+    (2048, 4, ra.SPLIT_STRIPED, 1, 2, 1, 64, 4, ra.F32),
+    (4096, 4, ra.SPLIT_ZIGZAG, 1, 4, 1, 128, 4, ra.BF16),
+])
+def test_split_pass_matches_oracle_and_counts(S, c, split, B, Hq, Hkv, d, n_splits, out_dtype):
+    """Concurrent groups of blocks folded by the merge: same result as the
+    oracle, same work counters as the single pass."""
+    p = Problem(S, c, split, B, Hq, Hkv, d, "bf16", seed=S + n_splits)
+    odt = torch.float32 if out_dtype == ra.F32 else torch.bfloat16
+    n = S // c
+    work = torch.full((n_splits, B, Hq, n, d), float("nan"), dtype=torch.float32, device=DEV)
+    work_l = torch.full((n_splits, B, Hq, n), float("nan"), dtype=torch.float32, device=DEV)
+    for r in range(c):
+        say(f"split pass S={S} c={c} rank {r} splits {n_splits}")
+        owners = p.ring_owners(r)
+        out = torch.full((B, Hq, n, d), float("nan"), dtype=odt, device=DEV)
+        lse = torch.full((B, Hq, n), float("nan"), dtype=torch.float32, device=DEV)
+        stats = torch.zeros(4, dtype=torch.int64, device=DEV)
+        ra.ring_attn_shard_fwd_split(p.desc(out_dtype), r, p.qs[r], [p.ks[j] for j in owners],
+                                     [p.vs[j] for j in owners], n_splits, work, work_l, out, lse,
+                                     block_owner=owners, stats=stats)
+        torch.cuda.synchronize()
+        ref_o, ref_l = p.reference(r)
+        compare(out, lse, ref_o, ref_l, tol=TOL["bf16"], bf16_out=out_dtype == ra.BF16)
+        _, _, s1 = p.run(r)
+        assert torch.equal(stats, s1), f"stats rank {r}"
+
+
 def test_bf16_output_mode():
     p = Problem(2048, 4, ra.SPLIT_ZIGZAG, 1, 4, 1, 128, "bf16", seed=11)
     for r in range(4):
