@@ -16,15 +16,22 @@
 //                     l when the max rises, exp2 in the log2 domain)
 //   O^T += V^T P^T   (V^T by transposing LDS reads, P^T from the registers).
 // The wave streams its range HBM -> LDS with LDS-direct buffer loads into a
-// private two-stage ring (no workgroup barriers): tile j+1 is in flight while
-// tile j is computed.  HBM-bound: K and V are read once.
+// private ring of tiles (no workgroup barriers): the next tiles are in flight
+// while tile j is computed.  HBM-bound: K and V are read once.
 #include "ra_common.h"
 #include "tile_common.h"
 
 namespace ra {
 namespace {
 
-constexpr int kDecWaves = 4;  // independent waves per workgroup
+#ifndef RA_DEC_WAVES
+#define RA_DEC_WAVES 4
+#endif
+#ifndef RA_DEC_STAGES
+#define RA_DEC_STAGES 2
+#endif
+constexpr int kDecWaves = RA_DEC_WAVES;    // independent waves per workgroup
+constexpr int kDecStages = RA_DEC_STAGES;  // tiles in each wave's LDS ring
 
 template <int D>
 __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(DecodeParams p) {
@@ -33,7 +40,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(DecodeParams p) 
   constexpr int TILEB = 32 * ROWB;         // one 32-key K or V tile
   constexpr int LOADS = TILEB / 1024;      // 1 KiB LDS-direct loads per tensor per tile
   constexpr int RPI = 1024 / ROWB;         // rows per load
-  constexpr int WAVEB = 2 * 2 * TILEB;     // two stages of K and V
+  constexpr int WAVEB = kDecStages * 2 * TILEB;  // the wave's ring of K and V tiles
+  static_assert(kDecStages >= 2 && kDecStages <= 4, "ring depth");
   __shared__ __attribute__((aligned(1024))) char smem[kDecWaves * WAVEB];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -83,7 +91,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(DecodeParams p) 
     for (int s = 0; s < D / 16; ++s) qreg[s] = col_ok ? *(const bf16x8*)(qp + s * 16) : bf16x8{};
   }
 
-  // Per-lane LDS read addresses in stage 0 (stage 1: + 2 * TILEB immediate).
+  // Per-lane LDS read addresses in stage 0 (stage s: + s * 2 * TILEB immediate).
   const uint32_t lds0 = (uint32_t)(uintptr_t)base;
   uint32_t kaddr[D / 16];
 #pragma unroll
@@ -103,14 +111,19 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(DecodeParams p) 
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
   float m = -INFINITY, l = 0.f;
 
-  if (n_tiles > 0) issue(0, 0);
-  if (n_tiles > 1) issue(1, 1);
+  for (int j = 0; j < kDecStages && j < n_tiles; ++j) issue(j, j);
 
   // One tile in LDS stage ST (compile-time, so the stage offset is an immediate).
   auto tile = [&](int j, auto ST) {
     constexpr int OFF = decltype(ST)::value * 2 * TILEB;
-    // Tile j has landed once at most the loads of tile j+1 remain.
-    if (j + 1 < n_tiles) {
+    // The ring holds tiles j .. j+kDecStages-1: tile j has landed once at
+    // most the loads of the later ones remain.
+    const int later = min(kDecStages - 1, n_tiles - 1 - j);
+    if (later >= 3) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(6 * LOADS) : "memory");
+    } else if (later == 2) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * LOADS) : "memory");
+    } else if (later == 1) {
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS) : "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -136,7 +149,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(DecodeParams p) 
     static_for<0, D / 32>([&va](auto DB) {
       asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(va[DB][0]), "+v"(va[DB][1])::"memory");
     });
-    if (j + 2 < n_tiles) issue(j + 2, decltype(ST)::value);
+    // Tile j is in registers: its stage takes tile j+kDecStages.
+    if (j + kDecStages < n_tiles) issue(j + kDecStages, decltype(ST)::value);
     f32x16 sacc = f32x16{};
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], qreg[s], sacc, 0, 0, 0);
@@ -175,9 +189,10 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(DecodeParams p) 
       oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][1], pb[1], oacc[db], 0, 0, 0);
     }
   };
-  for (int j = 0; j < n_tiles; j += 2) {
-    tile(j, Ic<0>{});
-    if (j + 1 < n_tiles) tile(j + 1, Ic<1>{});
+  for (int j = 0; j < n_tiles; j += kDecStages) {
+    static_for<0, kDecStages>([&](auto ST) {
+      if (j + decltype(ST)::value < n_tiles) tile(j + decltype(ST)::value, ST);
+    });
   }
 
   // out = O / l for the group's heads; lse = ln 2 * (m + log2 l).
