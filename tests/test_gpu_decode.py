@@ -82,6 +82,14 @@ def test_decode_parts_and_merge(S, c, split, B, Hq, Hkv, d, n_splits):
     compare(out[:, :, None], lse[:, :, None], ref_o, ref_l, tol=TOL["bf16"])
 
 
+def test_decode_maximum_block_count():
+    p = Decode(8192, 128, ra.SPLIT_ZIGZAG, 1, 8, 1, 128, seed=9)
+    outs, lses = p.run(list(range(128)), 2)
+    out, lse = p.merged(outs, lses)
+    ref_o, ref_l = p.ref()
+    compare(out[:, :, None], lse[:, :, None], ref_o, ref_l, tol=TOL["bf16"])
+
+
 def test_decode_block_subset_in_given_order():
     """A device holding some blocks: parts follow the blocks in the order given."""
     p = Decode(4096, 8, ra.SPLIT_ZIGZAG, 1, 8, 2, 128, seed=5)

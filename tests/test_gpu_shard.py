@@ -137,6 +137,21 @@ def test_split_pass_matches_oracle_and_counts(S, c, split, B, Hq, Hkv, d, n_spli
         assert torch.equal(stats, s1), f"stats rank {r}"
 
 
+@pytest.mark.parametrize("split", [ra.SPLIT_ZIGZAG, ra.SPLIT_CONTIGUOUS])
+def test_maximum_block_count(split):
+    """RA_MAX_BLOCKS (128) ring blocks in one call: every row of three ranks,
+    and the work counters."""
+    S, c = 16384, 128
+    p = Problem(S, c, split, 1, 2, 1, 128, "bf16", seed=77)
+    tq, tk = ra.ring_attn_tile_shape(p.desc())
+    for r in (0, 63, 127):
+        say(f"128 blocks split {split} rank {r}")
+        out, lse, stats = p.run(r)
+        ref_o, ref_l = p.reference(r)
+        compare(out, lse, ref_o, ref_l, tol=TOL["bf16"])
+        assert stats.cpu().tolist() == expected_stats(p, r, tq, tk), f"stats rank {r}"
+
+
 def test_bf16_output_mode():
     p = Problem(2048, 4, ra.SPLIT_ZIGZAG, 1, 4, 1, 128, "bf16", seed=11)
     for r in range(4):
