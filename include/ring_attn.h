@@ -119,7 +119,8 @@ ra_status zigzag_unpartition(int64_t seq_len, int32_t n_shards, int32_t split,
 /* One shard's queries against a sequence of key/value blocks.
  *
  * rank         : the shard r in [0, c) whose queries q holds.
- * q            : device [B, h_q, S/c, d] in_dtype, shard r's tokens in shard order.
+ * q            : device [B, h_q, S/c, d] in_dtype, shard r's tokens in shard order
+ *                ([B, h_q, S, d] in natural order with RA_FLAG_NATURAL_QO).
  * n_blocks     : number of blocks to fold, 1..min(c, RA_MAX_BLOCKS).
  * block_owner  : host int32[n_blocks], the shard each block belongs to, in
  *                visiting order; distinct values in [0, c).  NULL = ring
@@ -128,10 +129,12 @@ ra_status zigzag_unpartition(int64_t seq_len, int32_t n_shards, int32_t split,
  * k_blocks,
  * v_blocks     : host arrays of n_blocks device pointers; block t is shard
  *                block_owner[t]'s keys / values, [B, h_kv, S/c, d] in_dtype.
- * out          : device [B, h_q, S/c, d] out_dtype.  With all c blocks it is
+ * out          : device [B, h_q, S/c, d] out_dtype ([B, h_q, S, d] with
+ *                RA_FLAG_NATURAL_QO: only shard r's rows are written).  With all c blocks it is
  *                the exact attention output of the shard's queries; with a
  *                subset, the partial result over those keys only.
- * lse          : device fp32 [B, h_q, S/c]: natural log of the sum of
+ * lse          : device fp32 [B, h_q, S/c] ([B, h_q, S] with
+ *                RA_FLAG_NATURAL_QO): natural log of the sum of
  *                exp(scale * q.k) over the visible keys of the folded
  *                blocks; -inf (with out = 0) for a row that sees none.
  * stats        : device int64[4] or NULL; atomically ADDED to:
@@ -169,9 +172,10 @@ ra_status ring_attn_tile_shape(const ra_attn_desc* desc, int32_t* tile_q, int32_
  *         (in-place accumulation); no other overlap is allowed.
  * Errors: RA_EINVAL for n_parts not in 1..RA_MAX_PARTS, any size < 1, null or
  *   misaligned pointers, unknown dtypes; RA_EUNSUPPORTED for head_dim that is
- *   not a multiple of 4 dividing 256 (each row is then handled inside one
- *   wavefront, which is what makes the in-place aliasing safe); RA_EHIP on
- *   launch failure. */
+ *   not a multiple of 4 dividing 256 (every row is then covered by whole
+ *   4-element groups, and each group is written only by the thread that read
+ *   it, which is what makes the in-place aliasing safe); RA_EHIP on launch
+ *   failure. */
 ra_status ring_attn_merge(int32_t batch, int32_t heads, int64_t rows, int32_t head_dim,
                           int32_t n_parts, const void* const* outs, int32_t parts_dtype,
                           const float* const* lses, void* out, int32_t out_dtype, float* lse,
