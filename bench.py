@@ -203,6 +203,8 @@ def main():
                      "traffic": measured_traffic() if w.name == "s128k_c16_zigzag_16x1" else None,
                      "kernel": "fwd_bf16_kernel" if w.dtype == "bf16" else "fwd_f32_kernel",
                      "flop_per_launch": flop_launch, "avg_launch_ms": round(avg_kernel_s * 1e3, 4),
+                     "median_launch_ms": round(float(np.median(kernel_ms)), 4),
+                     "min_launch_ms": round(float(np.min(kernel_ms)), 4),
                      "launches_timed": len(kernel_ms),
                      "probe_sustained_tflops": round(probe_tf, 1),
                      "frac_of_probe": round(achieved / probe_tf, 4),
