@@ -5,9 +5,10 @@
 // (running max, normaliser, rescale when the max rises; "Sequence / context
 // parallelism" notes, section 4; "Sequence Parallelism and Ring Attention
 // Quiz", Q3 and Q7).  Blocks that would arrive over the ring are streamed
-// HBM -> LDS by the buffer unit's LDS-direct loads (no register staging),
-// the next tile in flight while the current one is computed (double-buffered
-// LDS).  The causal mask is resolved per (block, tile) from token positions:
+// HBM -> LDS by the buffer unit's LDS-direct loads (no register staging)
+// into a six-stage ring, so that the tiles after the one being computed are
+// already in flight (the prefetch that hides the ring's transfers).  The
+// causal mask is resolved per (block, tile) from token positions:
 // tiles entirely after the query tile are never loaded, tiles entirely before
 // it run unmasked, and only tiles that straddle the diagonal (or the shard
 // end) apply an elementwise mask.
@@ -41,7 +42,10 @@
 // contiguous, zig-zag and striped placement alike, so every workgroup does the
 // same work (the zig-zag balancing idea applied to tiles inside one shard).
 // Consecutive workgroup ids are placed on one XCD, so the query heads that
-// share a key/value head stream the same K/V through one L2.
+// share a key/value head stream the same K/V through one L2.  The grid may
+// also be split over groups of blocks (each group writes a partial result to
+// be merged), and q / out / lse may be addressed at global token positions of
+// natural-order tensors instead of shard order.
 #include <type_traits>
 
 #include "ra_common.h"
