@@ -69,6 +69,22 @@ def cpu_baseline(w, target_s):
                       f"({flop / 1e9:.1f} GFLOP useful in {elapsed:.1f} s, fp64, timed around the oracle call)"}
 
 
+def cpu_baseline_full(w):
+    """The fp64 oracle over the whole problem of a small workload: full causal
+    attention of every query head over the natural-order sequence (every
+    shard's rows at once)."""
+    import oracle
+    q, k, v = workloads.draw_qkv(w)
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, w.scale, w.causal)
+    elapsed = time.perf_counter() - t0
+    pairs = w.seq_len * (w.seq_len + 1) // 2 if w.causal else w.seq_len * w.seq_len
+    flop = useful_flop(w, pairs)
+    return {"seconds": elapsed, "value": flop / elapsed / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle", "sample": f"whole problem: {w.batch * w.h_q * w.seq_len} (query row, head) items, "
+                                        f"{flop / 1e9:.2f} GFLOP useful, fp64"}
+
+
 def measured_traffic():
     """HBM bytes per attention launch from the committed counter summary, or
     None when the kernel source has changed since the counters were taken."""
@@ -95,7 +111,8 @@ def main():
     ap.add_argument("--suite", action="store_true",
                     help="instead of the headline line, print one JSON line per secondary measurement: "
                          "MFMA probe, per-shard balance (32k tokens), warm/cold and overlap on/off "
-                         "(131k tokens), partial+merge and bidirectional passes (262k tokens)")
+                         "(131k tokens), partial+merge and bidirectional passes (262k tokens), split-KV "
+                         "decode, and every workload's GPU time beside the fp64 oracle's")
     ap.add_argument("--reps", type=int, default=5, help="repetitions per timed launch in --suite")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -328,6 +345,8 @@ def suite(args):
     split_suite(torch, ra, dev, reps)
     natural_step_suite(torch, ra, dev, reps)
     decode_suite(torch, ra, dev, reps)
+    if args.cpu_seconds > 0:
+        oracle_suite(torch, ra, dev, reps, min(args.cpu_seconds, 4.0))
 
     # 262 144 tokens, c = 32, 64/8 heads, shard 0: fused pass, per-block partials
     # folded by 31 two-way merges, and the bidirectional (non-causal) pass.
@@ -486,6 +505,49 @@ def decode_suite(torch, ra, dev, reps):
               "partials": n_parts, "decode": sd, "merge": sm, "decode_plus_merge": st,
               "decode_roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
                                   "frac": round(gbs / 8000.0, 4), "bytes": byts}})
+
+
+def oracle_suite(torch, ra, dev, reps, sample_s):
+    """GPU time beside the fp64 oracle's time for every workload (a CPU
+    baseline only).  Workloads of at most 8 192 tokens: the whole problem, i.e.
+    every shard's ring pass on the GPU against full attention over the sequence
+    in the oracle.  Larger ones: shard 0's pass on the GPU; the oracle timed on
+    a bounded row sample (cpu_baseline) and scaled to the shard's useful FLOP
+    (marked extrapolated)."""
+    for w in workloads.WORKLOADS:
+        c, n = w.n_shards, w.n_loc
+        whole = w.seq_len <= 8192
+        ranks = list(range(c)) if whole else [0]
+        dt, in_dt = (torch.bfloat16, ra.BF16) if w.dtype == "bf16" else (torch.float32, ra.F32)
+        g = torch.Generator(device=dev).manual_seed(w.seed)
+        rnd = lambda *shape: (torch.randn(shape, generator=g, device=dev) * w.sigma).to(dt)  # noqa: E731
+        qs = {r: rnd(w.batch, w.h_q, n, w.head_dim) for r in ranks}
+        ks, vs = rnd(c, w.batch, w.h_kv, n, w.head_dim), rnd(c, w.batch, w.h_kv, n, w.head_dim)
+        out = torch.empty((w.batch, w.h_q, n, w.head_dim), dtype=dt, device=dev)
+        lse = torch.empty((w.batch, w.h_q, n), dtype=torch.float32, device=dev)
+        desc = ra.make_desc(w.seq_len, c, w.split, w.batch, w.h_q, w.h_kv, w.head_dim, in_dt, in_dt, w.causal,
+                            w.scale)
+        own = {r: [(r - t) % c for t in range(c)] for r in ranks}
+
+        def run():
+            for r in ranks:
+                ra.ring_attn_shard_fwd(desc, r, qs[r], [ks[j] for j in own[r]], [vs[j] for j in own[r]], out, lse)
+
+        st = stat(timed(torch, run, reps))
+        flop = sum(useful_flop(w, shard_pairs(w, r)) for r in ranks)
+        del qs, ks, vs, out, lse
+        if whole:
+            cb = cpu_baseline_full(w)
+            oracle_s = cb.pop("seconds")
+        else:
+            cb = cpu_baseline(w, sample_s)
+            oracle_s = flop / (cb["value"] * 1e12)
+        gpu_s = st["median_ms"] / 1e3
+        emit({"measurement": "gpu_vs_oracle", "workload": w.name,
+              "scope": f"all {c} shards" if whole else "shard 0", "useful_flop": flop,
+              "gpu": {**st, "tflops": round(flop / gpu_s / 1e12, 3)},
+              "oracle": {"seconds": round(oracle_s, 3), "extrapolated": not whole, **cb},
+              "gpu_speedup_over_oracle": round(oracle_s / gpu_s, 1)})
 
 
 def shard_pairs(w, r):

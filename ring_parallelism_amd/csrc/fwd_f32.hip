@@ -1,4 +1,4 @@
-// fp32 shard forward: plain VALU kernel, one query row per lane.
+// fp32 shard forward: plain VALU kernel, one query row per four lanes.
 //
 // The online-softmax fold over ring-ordered key/value blocks ("Sequence /
 // context parallelism" notes, section 4): per key tile, raise the running
@@ -7,12 +7,13 @@
 // the end.  Everything stays in fp32 (no reduced-precision products), which
 // is what a 1e-5 absolute bound against fp64 needs.
 //
-// Workgroup = one wavefront = the query rows of one (batch, head): 64 rows at
-// d = 64, one per lane; 32 rows at d = 128, each split over lanes l and l + 32
-// (64 dimensions each, the two halves of every score added with one lane
-// swap), so that a lane's query and output rows stay in registers.  Key/value
-// tiles of TK rows are staged in LDS and read as broadcasts.  Tiles whose
-// keys all follow the workgroup's last query are skipped without being read.
+// Workgroup = one wavefront = 16 query rows of one (batch, head); each row
+// is spread over 4 lanes (lanes l, l+16, l+32, l+48), each holding d/4 of its
+// dimensions, and a score is the sum of the 4 partial dot products (two lane
+// exchanges), so every lane of a row holds the whole score.  Small rows per
+// wave keep many workgroups in flight on small shards.  Key/value tiles of TK
+// rows are staged in LDS and read as broadcasts.  Tiles whose keys all follow
+// the workgroup's last query are skipped without being read.
 #include "ra_common.h"
 #include "tile_common.h"
 
@@ -20,14 +21,12 @@ namespace ra {
 namespace {
 
 constexpr int TK = 32;
-constexpr int kHalf = 64;  // dimensions held per lane
-template <int D>
-constexpr int rows_per_wave() { return 64 / (D / kHalf); }
+constexpr int kLanesPerRow = 4;
+constexpr int TQ = 64 / kLanesPerRow;  // query rows per wavefront
 
 template <int D>
 __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
-  constexpr int SPLIT = D / kHalf;  // lanes per query row
-  constexpr int TQ = rows_per_wave<D>();
+  constexpr int DL = D / kLanesPerRow;  // dimensions held per lane
   __shared__ float ks[TK][D];
   __shared__ float vs[TK][D];
 
@@ -39,8 +38,8 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
   const int hk = h / p.group;
   const int64_t n_loc = p.n_loc;
 
-  const int part = lane / TQ;  // which 64 dimensions of the row this lane holds
-  const int d0 = part * kHalf;
+  const int part = lane / TQ;  // which quarter of the row's dimensions this lane holds
+  const int d0 = part * DL;
   const int64_t i0 = (int64_t)qt * TQ;
   const int64_t row = i0 + lane % TQ;
   const bool row_ok = row < n_loc;
@@ -52,9 +51,9 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
 
   const int64_t qrow = row_ok ? (p.qo_natural ? pos_q : row) : 0;  // q / out / lse row of this query
   const float* qp = (const float*)p.q + (((int64_t)b * p.h_q + h) * p.qo_rows + qrow) * D;
-  float qv[kHalf], o[kHalf];
+  float qv[DL], o[DL];
 #pragma unroll
-  for (int e = 0; e < kHalf; ++e) {
+  for (int e = 0; e < DL; ++e) {
     qv[e] = row_ok ? qp[d0 + e] : 0.f;
     o[e] = 0.f;
   }
@@ -77,11 +76,15 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
     for (int kt = 0; kt < n_vis; ++kt) {
       const int64_t key0 = (int64_t)kt * TK;
       __syncthreads();
-      for (int idx = lane; idx < TK * D; idx += 64) {
-        const int kk = idx / D, e = idx % D;
+      for (int idx = lane; idx < TK * D / 4; idx += 64) {
+        const int kk = idx / (D / 4), e = (idx % (D / 4)) * 4;
+        // Rows past the shard end read row 0 (always present) and store zeros.
         const bool ok = key0 + kk < n_loc;
-        ks[kk][e] = ok ? kp[(key0 + kk) * D + e] : 0.f;
-        vs[kk][e] = ok ? vp[(key0 + kk) * D + e] : 0.f;
+        const int64_t kr = ok ? key0 + kk : 0;
+        const float4 kx = *(const float4*)(kp + kr * D + e);
+        const float4 vx = *(const float4*)(vp + kr * D + e);
+        *(float4*)&ks[kk][e] = float4{ok ? kx.x : 0.f, ok ? kx.y : 0.f, ok ? kx.z : 0.f, ok ? kx.w : 0.f};
+        *(float4*)&vs[kk][e] = float4{ok ? vx.x : 0.f, ok ? vx.y : 0.f, ok ? vx.z : 0.f, ok ? vx.w : 0.f};
       }
       __syncthreads();
 
@@ -92,8 +95,10 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
       for (int kk = 0; kk < TK; ++kk) {
         float dot = 0.f;
 #pragma unroll
-        for (int e = 0; e < kHalf; ++e) dot = fmaf(qv[e], ks[kk][d0 + e], dot);
-        if constexpr (SPLIT == 2) dot = halves_sum(dot);  // both halves hold the full score
+        for (int e = 0; e < DL; ++e) dot = fmaf(qv[e], ks[kk][d0 + e], dot);
+        // Every lane of the row ends with the full score.
+        dot += __shfl_xor(dot, TQ);
+        dot += __shfl_xor(dot, 2 * TQ);
         bool vis = true;
         if (masked) {
           const int64_t jj = key0 + kk;
@@ -110,13 +115,13 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
       const float alpha = expf(m - m_new);  // m = -inf gives 0
       l *= alpha;
 #pragma unroll
-      for (int e = 0; e < kHalf; ++e) o[e] *= alpha;
+      for (int e = 0; e < DL; ++e) o[e] *= alpha;
 #pragma unroll 4
       for (int kk = 0; kk < TK; ++kk) {
         const float pk = expf(s[kk] - m_new);
         l += pk;
 #pragma unroll
-        for (int e = 0; e < kHalf; ++e) o[e] = fmaf(pk, vs[kk][d0 + e], o[e]);
+        for (int e = 0; e < DL; ++e) o[e] = fmaf(pk, vs[kk][d0 + e], o[e]);
       }
       m = m_new;
     }
@@ -127,7 +132,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
     float* op = (float*)p.out + ro * D;
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-    for (int e = 0; e < kHalf; ++e) op[d0 + e] = o[e] * inv;
+    for (int e = 0; e < DL; ++e) op[d0 + e] = o[e] * inv;
     if (part == 0) p.lse[ro] = l > 0.f ? m + logf(l) : -INFINITY;
   }
 
@@ -145,14 +150,13 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
 
 }  // namespace
 
-void tile_shape_f32(int32_t head_dim, int32_t* tq, int32_t* tk) {
-  *tq = head_dim == 64 ? rows_per_wave<64>() : rows_per_wave<128>();
+void tile_shape_f32(int32_t /*head_dim*/, int32_t* tq, int32_t* tk) {
+  *tq = TQ;
   *tk = TK;
 }
 
 hipError_t launch_fwd_f32(const FwdParams& p0, int32_t head_dim, hipStream_t stream) {
   FwdParams p = p0;
-  const int TQ = head_dim == 64 ? rows_per_wave<64>() : rows_per_wave<128>();
   p.n_qtiles = (int32_t)((p.n_loc + TQ - 1) / TQ);
   p.n_ktiles = (int32_t)((p.n_loc + TK - 1) / TK);
   p.n_pairs = p.n_qtiles;

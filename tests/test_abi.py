@@ -69,8 +69,8 @@ def expect(status, fn, *a, match=None, **kw):
 def test_tile_shape():
     tq, tk = ra.ring_attn_tile_shape(good_desc())
     assert tq % 32 == 0 and tq >= 64 and tk in (32, 64)
-    assert ra.ring_attn_tile_shape(good_desc(in_dtype=ra.F32, head_dim=64)) == (64, 32)
-    assert ra.ring_attn_tile_shape(good_desc(in_dtype=ra.F32, head_dim=128)) == (32, 32)
+    assert ra.ring_attn_tile_shape(good_desc(in_dtype=ra.F32, head_dim=64)) == (16, 32)
+    assert ra.ring_attn_tile_shape(good_desc(in_dtype=ra.F32, head_dim=128)) == (16, 32)
 
 
 @pytest.mark.parametrize("kw,status,match", [
