@@ -117,7 +117,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the ring: run with --gpus 1 (got {args.gpus}); "
-              "the multi-GPU ring is not part of this build", file=sys.stderr)
+              "the multi-GPU ring is not implemented here", file=sys.stderr)
         sys.exit(2)
 
     import torch
