@@ -38,6 +38,11 @@ __device__ inline float halves_sum(float x) {
 __device__ inline void lds_load16(__amdgpu_buffer_rsrc_t r, lds_char* dst, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
 }
+// The same with the non-temporal (streaming) cache policy (cache-policy
+// operand bit 1, "nt"), for data that is read once.
+__device__ inline void lds_load16_nt(__amdgpu_buffer_rsrc_t r, lds_char* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 2);
+}
 
 template <int V>
 using Ic = std::integral_constant<int, V>;

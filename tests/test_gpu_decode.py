@@ -138,3 +138,30 @@ def test_strided_merge_in_place_matches_pointer_merge():
     fin = np.isfinite(ref_l)
     assert np.abs(lse.cpu().numpy()[fin] - ref_l[fin]).max() < 1e-5
     assert np.all(np.isneginf(lse.cpu().numpy()[~fin]))
+
+
+@pytest.mark.parametrize("n_parts,in_place", [(40, False), (40, True), (19, False)])
+def test_many_part_merge_vs_oracle(n_parts, in_place):
+    """Many parts over few rows (the split-KV shape: the library spreads each
+    group's parts over several threads unless lse is written over part 0's)."""
+    g = torch.Generator(device=DEV).manual_seed(n_parts)
+    B, H, R, d = 1, 6, 3, 128
+    outs = torch.randn((n_parts, B, H, R, d), generator=g, device=DEV)
+    lses = torch.randn((n_parts, B, H, R), generator=g, device=DEV) * 6
+    lses[::3, 0, 1, 0] = float("-inf")   # parts without keys for one row
+    lses[:, 0, 4, 2] = float("-inf")     # a row with no keys in any part
+    ref_o, ref_l = oracle.merge([x.cpu().numpy().astype(np.float64) for x in outs],
+                                [x.cpu().numpy().astype(np.float64) for x in lses])
+    if in_place:
+        ra.ring_attn_merge_strided(B, H, R, d, outs, ra.F32, lses, outs[0], ra.F32, lses[0])
+        out, lse = outs[0], lses[0]
+    else:
+        out = torch.empty((B, H, R, d), device=DEV)
+        lse = torch.empty((B, H, R), device=DEV)
+        ra.ring_attn_merge_strided(B, H, R, d, outs, ra.F32, lses, out, ra.F32, lse)
+    torch.cuda.synchronize()
+    assert np.abs(out.cpu().numpy() - ref_o).max() < 1e-5
+    fin = np.isfinite(ref_l)
+    assert np.abs(lse.cpu().numpy()[fin] - ref_l[fin]).max() < 1e-5
+    assert np.all(np.isneginf(lse.cpu().numpy()[~fin]))
+    assert np.all(out.cpu().numpy()[0, 4, 2] == 0)
