@@ -12,23 +12,35 @@
 // dimensions, and a score is the sum of the 4 partial dot products (two lane
 // exchanges), so every lane of a row holds the whole score.  Small rows per
 // wave keep many workgroups in flight on small shards.  Key/value tiles of TK
-// rows are staged in LDS and read as broadcasts.  Tiles whose keys all follow
-// the workgroup's last query are skipped without being read.
+// rows are staged in LDS (two buffers: the next tile's loads are in flight
+// while a tile is computed) and read as broadcasts.  Tiles whose keys all
+// follow the workgroup's last query are skipped without being read.
 #include "ra_common.h"
 #include "tile_common.h"
 
 namespace ra {
 namespace {
 
+// Sum over lanes l and l ^ 16 (the 16-lane rows of each half-wave swapped):
+// as with halves_sum, both lanes of a pair get the same value bit for bit.
+__device__ inline float rows16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 constexpr int TK = 32;
 constexpr int kLanesPerRow = 4;
 constexpr int TQ = 64 / kLanesPerRow;  // query rows per wavefront
+static_assert(kLanesPerRow == 4, "the score reduction pairs lanes l ^ 16 and l ^ 32");
 
 template <int D>
 __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
   constexpr int DL = D / kLanesPerRow;  // dimensions held per lane
-  __shared__ float ks[TK][D];
-  __shared__ float vs[TK][D];
+  constexpr int NL = TK * D / 4 / 64;  // 16-byte loads per lane per tile and tensor
+  // Two LDS buffers: tile kt+1 is loaded into registers while tile kt is
+  // computed, then stored into the other buffer.
+  __shared__ float ks[2][TK][D];
+  __shared__ float vs[2][TK][D];
 
   const int lane = threadIdx.x;
   const int w = blockIdx.x;
@@ -73,20 +85,44 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
     t_part += n_vis - n_full;
     t_skip += p.n_ktiles - n_vis;
 
+    // Tile kt's K and V rows in registers; rows past the shard end read row 0
+    // (always present) and are stored as zeros.
+    float4 kx[NL], vx[NL];
+    auto load = [&](int kt) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int idx = lane + 64 * i;
+        const int kk = idx / (D / 4), e = (idx % (D / 4)) * 4;
+        const int64_t key = (int64_t)kt * TK + kk;
+        const int64_t kr = key < n_loc ? key : 0;
+        kx[i] = *(const float4*)(kp + kr * D + e);
+        vx[i] = *(const float4*)(vp + kr * D + e);
+      }
+    };
+    auto store = [&](int kt, int buf) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int idx = lane + 64 * i;
+        const int kk = idx / (D / 4), e = (idx % (D / 4)) * 4;
+        const bool ok = (int64_t)kt * TK + kk < n_loc;
+        *(float4*)&ks[buf][kk][e] =
+            float4{ok ? kx[i].x : 0.f, ok ? kx[i].y : 0.f, ok ? kx[i].z : 0.f, ok ? kx[i].w : 0.f};
+        *(float4*)&vs[buf][kk][e] =
+            float4{ok ? vx[i].x : 0.f, ok ? vx[i].y : 0.f, ok ? vx[i].z : 0.f, ok ? vx[i].w : 0.f};
+      }
+    };
+    if (n_vis > 0) load(0);
+
     for (int kt = 0; kt < n_vis; ++kt) {
       const int64_t key0 = (int64_t)kt * TK;
-      __syncthreads();
-      for (int idx = lane; idx < TK * D / 4; idx += 64) {
-        const int kk = idx / (D / 4), e = (idx % (D / 4)) * 4;
-        // Rows past the shard end read row 0 (always present) and store zeros.
-        const bool ok = key0 + kk < n_loc;
-        const int64_t kr = ok ? key0 + kk : 0;
-        const float4 kx = *(const float4*)(kp + kr * D + e);
-        const float4 vx = *(const float4*)(vp + kr * D + e);
-        *(float4*)&ks[kk][e] = float4{ok ? kx.x : 0.f, ok ? kx.y : 0.f, ok ? kx.z : 0.f, ok ? kx.w : 0.f};
-        *(float4*)&vs[kk][e] = float4{ok ? vx.x : 0.f, ok ? vx.y : 0.f, ok ? vx.z : 0.f, ok ? vx.w : 0.f};
-      }
-      __syncthreads();
+      const int buf = kt & 1;
+      // Buffer `buf` was last read by tile kt-2 (or by the previous block's
+      // tiles), whose reads ended before an earlier barrier: the one after
+      // tile kt-1 was stored, or for tile 0 the one here.
+      if (kt == 0) __syncthreads();
+      store(kt, buf);
+      __syncthreads();  // tile kt visible to every lane
+      if (kt + 1 < n_vis) load(kt + 1);  // in flight while tile kt is computed
 
       const bool masked = kt >= n_full;
       float s[TK];
@@ -95,10 +131,9 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
       for (int kk = 0; kk < TK; ++kk) {
         float dot = 0.f;
 #pragma unroll
-        for (int e = 0; e < DL; ++e) dot = fmaf(qv[e], ks[kk][d0 + e], dot);
-        // Every lane of the row ends with the full score.
-        dot += __shfl_xor(dot, TQ);
-        dot += __shfl_xor(dot, 2 * TQ);
+        for (int e = 0; e < DL; ++e) dot = fmaf(qv[e], ks[buf][kk][d0 + e], dot);
+        // Every lane of the row ends with the full score, bit for bit.
+        dot = halves_sum(rows16_sum(dot));
         bool vis = true;
         if (masked) {
           const int64_t jj = key0 + kk;
@@ -121,7 +156,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
         const float pk = expf(s[kk] - m_new);
         l += pk;
 #pragma unroll
-        for (int e = 0; e < DL; ++e) o[e] = fmaf(pk, vs[kk][d0 + e], o[e]);
+        for (int e = 0; e < DL; ++e) o[e] = fmaf(pk, vs[buf][kk][d0 + e], o[e]);
       }
       m = m_new;
     }
