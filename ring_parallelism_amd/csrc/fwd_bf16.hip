@@ -260,12 +260,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       }
     };
 
-    // S^T = K Q^T for the tile in stage S: eight 16-wide slices of d, four
-    // K reads in flight ahead of the products (lgkmcnt counts LDS reads in
-    // issue order; the wait before slice s allows the reads issued after it).
+    // S^T = K Q^T for the tile in stage S: D/16 16-wide slices of d, up to
+    // six K reads in flight ahead of the products (measured best of 2..8 at
+    // d = 128; lgkmcnt counts LDS reads in issue order, and the wait before
+    // slice s allows the reads issued after it).
     auto qk = [&](f32x16 (&sacc)[MB][NB], auto S) {
       constexpr int OFF = decltype(S)::value * C::TILEB;
-      constexpr int NR = D / 16, PF = 4;
+      constexpr int NR = D / 16, PF = NR < 6 ? NR : 6;
       bf16x8 a[NR];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) sacc[0][nb] = f32x16{};
