@@ -7,7 +7,9 @@
 // Quiz", Q3 and Q7).  Blocks that would arrive over the ring are streamed
 // HBM -> LDS by the buffer unit's LDS-direct loads (no register staging)
 // into a six-stage ring, so that the tiles after the one being computed are
-// already in flight (the prefetch that hides the ring's transfers).  The
+// already in flight (the prefetch that hides the ring's transfers); a tile's
+// K fragments move on from LDS into registers one step before its score
+// products.  The
 // causal mask is resolved per (block, tile) from token positions:
 // tiles entirely after the query tile are never loaded, tiles entirely before
 // it run unmasked, and only tiles that straddle the diagonal (or the shard
@@ -440,13 +442,51 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       });
     };
 
+    // With paired steps the K fragments of tile i+2 are read into registers
+    // during the value product of step i (that tile landed before the barrier
+    // closing step i-1): the score products of step i+1 then start without an
+    // LDS wait, and a step's LDS reads split between its halves -- V beside
+    // the score products, K beside the value product.
+    auto k_reads = [&kaddr](auto S, bf16x8 (&kf)[D / 16]) {
+      constexpr int OFF = decltype(S)::value * C::TILEB;
+      static_for<0, D / 16>([&kaddr, &kf](auto I) {
+        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(kf[I]) : "v"(kaddr[I]), "n"(OFF));
+      });
+    };
+    // S^T = K Q^T from fragments read by k_reads a step earlier (the last LDS
+    // reads issued): one wait for all of them, so that the V reads issued next
+    // are not held behind per-slice waits.
+    auto qk_held = [&](f32x16 (&sacc)[MB][NB], bf16x8 (&kf)[D / 16]) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) sacc[0][nb] = f32x16{};
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int sl = 0; sl < D / 16; ++sl) asm volatile("" : "+v"(kf[sl]));
+#pragma unroll
+      for (int sl = 0; sl < D / 16; ++sl)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          sacc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sl], qreg[nb][sl], sacc[0][nb], 0, 0, 0);
+    };
+    // O^T += V^T P^T from V reads the caller has waited for (same order of
+    // products per accumulator as pv).
+    auto pv_held = [&](bf16x8 (&va)[D / 32][2 * MB], const bf16x8 (&pb)[NB][2 * MB]) {
+#pragma unroll
+      for (int k16 = 0; k16 < 2; ++k16)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            oacc[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][k16], pb[nb][k16], oacc[db][nb], 0, 0, 0);
+    };
+
     // Software pipeline over the tile sequence, C::STAGES LDS stages in a
     // ring.  Step i: the scores of tile i+1 run on the matrix cores beside
     // the exponentials of tile i on the vector unit; then the value product
-    // of tile i runs beside the shift of tile i+1.  Loads run STAGES-2 tiles
-    // ahead: with paired steps, every even step issues two tiles and every
-    // odd step ends with the workgroup barrier; otherwise one tile and one
-    // barrier per step.  Two cursors walk the tile list: `ld` (the tile being
+    // of tile i runs beside the shift of tile i+1 (and, with paired steps,
+    // the K reads of tile i+2).  Loads run STAGES-2 tiles ahead: with paired
+    // steps, every even step issues two tiles and every odd step ends with the
+    // workgroup barrier; otherwise one tile and one barrier per step.  Two cursors walk the tile list: `ld` (the tile being
     // loaded) and `nx` (tile i+1); n_tiles bounds both.
     constexpr int NS = C::STAGES;
     Tile first;
@@ -486,8 +526,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
     bf16x8 pb[NB][2 * MB], va[D / 32][2 * MB];
     float mt[NB], ls[NB];
     bool unset = false;
+    bf16x8 kf[D / 16];  // K fragments of the next tile (paired steps)
     if (n_tiles > 0) {
       qk(xa, Ic<0>{});
+      if constexpr (C::PAIRED) k_reads(Ic<1>{}, kf);
       if (first.kt >= first.full) mask(xa, first);
       row_max(xa, mt);
       shift(xa);
@@ -517,7 +559,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
         // Measurement mode: no overlap of the tile transfers with compute.
         if (p.sync_loads) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
-      qk(y, Ic<(k + 1) % NS>{});  // harmless when there is no tile i+1
+      // Scores of tile i+1 (harmless when there is no tile i+1).
+      if constexpr (C::PAIRED) {
+        qk_held(y, kf);
+      } else {
+        qk(y, Ic<(k + 1) % NS>{});
+      }
       v_reads(Ic<k % NS>{}, va);
       exps(x, pb, ls);
       bool over = false;
@@ -541,7 +588,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
         for (int k4 = 0; k4 < 2 * MB; ++k4) asm volatile("" : "+v"(pb[nb][k4]));
       if (has_next && nx.kt >= nx.full) mask(y, nx);
-      pv(va, pb);
+      if constexpr (C::PAIRED) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the V reads of tile i
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) asm volatile("" : "+v"(va[db][0]), "+v"(va[db][1]));
+        k_reads(Ic<(k + 2) % NS>{}, kf);  // tile i+2 (harmless past the end)
+        pv_held(va, pb);
+      } else {
+        pv(va, pb);
+      }
       shift(y);
       // Keep the shift beside the value product (left alone, it sinks into
       // the next step, where the vector unit already has the exponentials).
@@ -571,6 +626,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
     constexpr int kUnroll = NS % 2 == 0 ? NS : 2 * NS;
     while (i < n_tiles) {
       if (!unrolled_steps<0, kUnroll>(step)) break;
+    }
+    if constexpr (C::PAIRED) {
+      // The last K reads issued ahead are never consumed: wait for them while
+      // their registers are still reserved.
+      static_for<0, D / 16>([&kf](auto I) { asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kf[I])); });
     }
     if constexpr (C::PAIRED) {
       // A final barrier: the sequence may end between the paired barriers.
