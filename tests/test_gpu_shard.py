@@ -288,3 +288,24 @@ def test_merge_in_place_and_identity():
     torch.cuda.synchronize()
     # merging a part with no keys changes nothing (up to the exp(0) * x / 1 round trip)
     assert (a - a0).abs().max().item() <= 1e-6 and (la - la0).abs().max().item() <= 1e-6
+
+
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("c", [1, 2])
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_pipeline_ends_at_every_step(d, c, causal):
+    """Shard lengths 32 .. 480 (1 .. 15 visible 32-key tiles per block and one
+    or two query tiles per workgroup): the tile pipeline, unrolled over six
+    steps with K fragments read a step ahead, ends at every position of its
+    unrolled loop.  Every row of every rank against the oracle, and the work
+    counters."""
+    for n_loc in range(32, 481, 32):
+        S = n_loc * c
+        p = Problem(S, c, ra.SPLIT_CONTIGUOUS, 1, 2, 1, d, "bf16", seed=S + c + d)
+        tq, tk = ra.ring_attn_tile_shape(p.desc(causal=causal))
+        for r in range(c):
+            say(f"pipeline end: d {d} c {c} causal {causal} n_loc {n_loc} rank {r}")
+            out, lse, stats = p.run(r, causal=causal)
+            ref_o, ref_l = p.reference(r, causal=causal)
+            compare(out, lse, ref_o, ref_l, tol=TOL["bf16"])
+            assert stats.cpu().tolist() == expected_stats(p, r, tq, tk, causal), f"stats n_loc {n_loc} rank {r}"
