@@ -1,0 +1,62 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU guard, the useful-FLOP
+accounting against the oracle's pair counts, and the source-hash gate on the
+committed HBM-traffic figure."""
+import os
+import shutil
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+import oracle
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_shard_pairs_match_the_oracle_for_every_workload():
+    """bench.py's own placement arithmetic agrees with the oracle's partition
+    and pair counts on every workload and every shard."""
+    for w in workloads.WORKLOADS:
+        perm = oracle.partition_perm(w.seq_len, w.n_shards, w.split)
+        for r in range(w.n_shards):
+            pos = perm[r * w.n_loc:(r + 1) * w.n_loc]
+            want = int((pos + 1).sum()) if w.causal else w.n_loc * w.seq_len
+            assert bench.shard_pairs(w, r) == want, (w.name, r)
+
+
+def test_useful_flop_of_the_headline_shard():
+    """4 d H_q B pairs: 4.398e12 FLOP for one shard of the 131 072-token workload
+    (the pages' per-device attention work for that layer shape)."""
+    w = workloads.WORKLOAD_BY_NAME["s128k_c16_zigzag_16x1"]
+    pairs = bench.shard_pairs(w, 0)
+    n = w.seq_len // (2 * w.n_shards)
+    assert pairs == n * n * (2 * w.n_shards - 1) + n * (n + 1)
+    assert bench.useful_flop(w, pairs) == 4.0 * 128 * 16 * pairs
+    assert abs(bench.useful_flop(w, pairs) - 4.398e12) / 4.398e12 < 1e-3
+    assert len({bench.shard_pairs(w, r) for r in range(w.n_shards)}) == 1  # zig-zag: equal work
+
+
+def test_traffic_figure_is_gated_on_the_kernel_source(tmp_path, monkeypatch):
+    """The committed counter figure is reported only while the kernel source
+    it was measured on is unchanged."""
+    got = bench.measured_traffic()
+    assert got is not None and got > 1e8, "committed profile must match the current fwd_bf16.hip"
+    fake = tmp_path / "root"
+    (fake / "profiles").mkdir(parents=True)
+    (fake / "ring_parallelism_amd" / "csrc").mkdir(parents=True)
+    shutil.copy(os.path.join(ROOT, "profiles", "fwd_bf16_s128k_c16_zigzag_hbm_traffic.md"), fake / "profiles")
+    src = fake / "ring_parallelism_amd" / "csrc" / "fwd_bf16.hip"
+    shutil.copy(os.path.join(ROOT, "ring_parallelism_amd", "csrc", "fwd_bf16.hip"), src)
+    monkeypatch.setattr(bench, "ROOT", str(fake))
+    assert bench.measured_traffic() == got
+    src.write_text(src.read_text() + "\n// edited\n")
+    assert bench.measured_traffic() is None
