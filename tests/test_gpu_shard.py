@@ -6,6 +6,7 @@ import torch
 
 import oracle
 import ring_parallelism_amd as ra
+import workloads
 from gpu_util import DEV, TOL, Problem, compare, expected_stats, say, up
 
 pytestmark = pytest.mark.gpu
@@ -309,3 +310,29 @@ def test_pipeline_ends_at_every_step(d, c, causal):
             ref_o, ref_l = p.reference(r, causal=causal)
             compare(out, lse, ref_o, ref_l, tol=TOL["bf16"])
             assert stats.cpu().tolist() == expected_stats(p, r, tq, tk, causal), f"stats n_loc {n_loc} rank {r}"
+
+
+def test_half_million_token_shard_sampled():
+    """A 524 288-token shard (1 048 576 tokens, c = 2 zig-zag, one head, d =
+    128): key-tile offsets inside a block reach 2^27 bytes and a query row
+    sees up to a million keys.  Both ranks; chunk edges plus 56 uniform rows
+    of each against the oracle over their full visible key sets; the pair
+    counter exact (the oracle's per-shard pair count), and the tile classes
+    covering every (query tile, key tile, block) once (enumerating the
+    classes pair by pair is out of reach at this size)."""
+    S, c = 1 << 20, 2
+    p = Problem(S, c, ra.SPLIT_ZIGZAG, 1, 1, 1, 128, "bf16", seed=77)
+    tq, tk = ra.ring_attn_tile_shape(p.desc())
+    pairs = oracle.pair_counts(S, c, oracle.SPLIT_ZIGZAG)
+    n_tiles = -(-p.n_loc // tq) * -(-p.n_loc // tk) * c
+    for r in range(c):
+        say(f"half-million-token shard rank {r}")
+        out, lse, stats = p.run(r)
+        rows = workloads.sample_rows(p.n_loc, p.n_loc // 2, 56, 500 + r)
+        ref_o, ref_l = p.reference(r, rows=rows)
+        compare(out, lse, ref_o, ref_l, rows=rows, tol=TOL["bf16"])
+        st = stats.cpu().tolist()
+        assert st[0] == int(pairs[r]), f"pairs rank {r}: {st[0]} vs {int(pairs[r])}"
+        assert st[1] + st[2] + st[3] == n_tiles and st[2] > 0, f"tile classes rank {r}: {st}"
+        del out, lse, stats
+        torch.cuda.empty_cache()
