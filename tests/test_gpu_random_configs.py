@@ -58,3 +58,130 @@ def test_random_configuration(case):
     ref_o, ref_l = p.reference(k["rank"], causal=k["causal"], owners=owners)
     compare(out, lse, ref_o, ref_l, tol=TOL[k["dtype"]], bf16_out=k["bf16_out"])
     assert stats.cpu().tolist() == expected_stats(p, k["rank"], tq, tk, k["causal"], owners)
+
+
+def _split_cases(n=40, seed=2025):
+    g = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        split = SPLITS[int(g.integers(0, 3))]
+        c = int(g.integers(1, 9))
+        n_loc = int(g.integers(1, 1201))
+        if split == ra.SPLIT_ZIGZAG and n_loc % 2:
+            n_loc += 1
+        h_kv = int(g.integers(1, 3))
+        owners = [int(x) for x in g.permutation(c)[:int(g.integers(1, c + 1))]] if g.random() < 0.3 else None
+        n_blocks = len(owners) if owners else c
+        out.append(dict(S=n_loc * c, c=c, split=split, B=int(g.integers(1, 3)), h_q=h_kv * int(g.choice([1, 2, 4])),
+                        h_kv=h_kv, d=int(g.choice([64, 128])), causal=bool(g.random() < 0.75),
+                        bf16_out=bool(g.random() < 0.3), rank=int(g.integers(0, c)), owners=owners,
+                        n_splits=int(g.integers(1, n_blocks + 1)), seed=20_000 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _split_cases(), ids=lambda k: f"S{k['S']}_c{k['c']}_sp{k['split']}_h{k['h_q']}x{k['h_kv']}"
+                                                             f"_d{k['d']}_splits{k['n_splits']}_r{k['rank']}")
+def test_random_split_pass(case):
+    """The block list cut into concurrent groups folded by the merge: the
+    oracle's result over the visited blocks, and the single pass's counters."""
+    import torch
+    from gpu_util import DEV
+    k = case
+    say(f"random split pass {k}")
+    p = Problem(k["S"], k["c"], k["split"], k["B"], k["h_q"], k["h_kv"], k["d"], "bf16", seed=k["seed"])
+    r = k["rank"]
+    owners = k["owners"] if k["owners"] is not None else p.ring_owners(r)
+    out_dtype = ra.BF16 if k["bf16_out"] else ra.F32
+    odt = torch.bfloat16 if k["bf16_out"] else torch.float32
+    ns, n = k["n_splits"], p.n_loc
+    work = torch.full((ns, p.B, p.Hq, n, p.d), float("nan"), dtype=torch.float32, device=DEV)
+    work_l = torch.full((ns, p.B, p.Hq, n), float("nan"), dtype=torch.float32, device=DEV)
+    out = torch.full((p.B, p.Hq, n, p.d), float("nan"), dtype=odt, device=DEV)
+    lse = torch.full((p.B, p.Hq, n), float("nan"), dtype=torch.float32, device=DEV)
+    stats = torch.zeros(4, dtype=torch.int64, device=DEV)
+    desc = p.desc(out_dtype, k["causal"])
+    ra.ring_attn_shard_fwd_split(desc, r, p.qs[r], [p.ks[j] for j in owners], [p.vs[j] for j in owners], ns,
+                                 work, work_l, out, lse, block_owner=owners, stats=stats)
+    torch.cuda.synchronize()
+    ref_o, ref_l = p.reference(r, causal=k["causal"], owners=owners)
+    compare(out, lse, ref_o, ref_l, tol=TOL["bf16"], bf16_out=k["bf16_out"])
+    _, _, s1 = p.run(r, causal=k["causal"], owners=owners)
+    assert torch.equal(stats, s1)
+
+
+def _natural_cases(n=30, seed=2026):
+    g = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        split = SPLITS[int(g.integers(0, 3))]
+        c = int(g.integers(1, 7))
+        n_loc = int(g.integers(1, 501))
+        if split == ra.SPLIT_ZIGZAG and n_loc % 2:
+            n_loc += 1
+        h_kv = int(g.integers(1, 3))
+        dtype = "f32" if g.random() < 0.3 else "bf16"
+        out.append(dict(S=n_loc * c, c=c, split=split, B=int(g.integers(1, 3)), h_q=h_kv * int(g.choice([1, 3])),
+                        h_kv=h_kv, d=int(g.choice([64, 128])), dtype=dtype, causal=bool(g.random() < 0.75),
+                        rank=int(g.integers(0, c)), seed=30_000 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _natural_cases(), ids=lambda k: f"S{k['S']}_c{k['c']}_sp{k['split']}_h{k['h_q']}x{k['h_kv']}"
+                                                               f"_d{k['d']}_{k['dtype']}_r{k['rank']}")
+def test_random_natural_order_q_out(case):
+    """Q read and out / lse written at global positions of natural-order
+    tensors: the rank's rows equal its shard-layout result bit for bit, and
+    no other row is touched."""
+    import torch
+    from gpu_util import DEV, up
+    k = case
+    say(f"random natural q/out {k}")
+    p = Problem(k["S"], k["c"], k["split"], k["B"], k["h_q"], k["h_kv"], k["d"], k["dtype"], seed=k["seed"])
+    r = k["rank"]
+    owners = p.ring_owners(r)
+    out_nat = torch.full((p.B, p.Hq, p.S, p.d), float("nan"), dtype=torch.float32, device=DEV)
+    lse_nat = torch.full((p.B, p.Hq, p.S), float("nan"), dtype=torch.float32, device=DEV)
+    ra.ring_attn_shard_fwd(p.desc(ra.F32, k["causal"], flags=ra.FLAG_NATURAL_QO), r, up(p.q, k["dtype"]),
+                           [p.ks[j] for j in owners], [p.vs[j] for j in owners], out_nat, lse_nat, block_owner=owners)
+    o, l, _ = p.run(r, causal=k["causal"])
+    rows = torch.from_numpy(p.perm[r * p.n_loc:(r + 1) * p.n_loc]).to(DEV)
+    torch.cuda.synchronize()
+    assert torch.equal(out_nat[:, :, rows], o) and torch.equal(lse_nat[:, :, rows], l)
+    others = torch.ones(p.S, dtype=torch.bool, device=DEV)
+    others[rows] = False
+    assert torch.isnan(out_nat[:, :, others]).all() and torch.isnan(lse_nat[:, :, others]).all()
+
+
+def _decode_cases(n=30, seed=2027):
+    g = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        split = SPLITS[int(g.integers(0, 3))]
+        c = int(g.integers(1, 9))
+        n_loc = int(g.integers(1, 1501))
+        if split == ra.SPLIT_ZIGZAG and n_loc % 2:
+            n_loc += 1
+        h_kv = int(g.integers(1, 4))
+        blocks = [int(x) for x in g.permutation(c)[:int(g.integers(1, c + 1))]]
+        out.append(dict(S=n_loc * c, c=c, split=split, B=int(g.integers(1, 3)),
+                        h_q=h_kv * int(g.choice([1, 2, 7, 16, 32])), h_kv=h_kv, d=int(g.choice([64, 128])),
+                        blocks=blocks, n_splits=int(g.integers(1, min(9, n_loc) + 1)), seed=40_000 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _decode_cases(), ids=lambda k: f"S{k['S']}_c{k['c']}_sp{k['split']}_h{k['h_q']}x{k['h_kv']}"
+                                                              f"_d{k['d']}_nb{len(k['blocks'])}_splits{k['n_splits']}")
+def test_random_decode_and_strided_merge(case):
+    """Split-KV decode over a random subset of the blocks in random order:
+    every partial against its key range, and the strided merge of all of them
+    against attention of a token after the whole cache over those blocks."""
+    from test_gpu_decode import Decode, check_parts
+    k = case
+    say(f"random decode {k}")
+    p = Decode(k["S"], k["c"], k["split"], k["B"], k["h_q"], k["h_kv"], k["d"], seed=k["seed"])
+    outs, lses = p.run(k["blocks"], k["n_splits"])
+    check_parts(p, k["blocks"], k["n_splits"], outs, lses)
+    out, lse = p.merged(outs, lses)
+    keys = np.concatenate([p.perm[t * p.n:(t + 1) * p.n] for t in k["blocks"]])
+    ref_o, ref_l = p.ref(keys=keys)
+    compare(out[:, :, None], lse[:, :, None], ref_o, ref_l, tol=TOL["bf16"])
