@@ -6,9 +6,11 @@ order.  Every row of the chosen rank against the oracle restricted to the
 visited blocks' keys, and the work counters bit-exact."""
 import numpy as np
 import pytest
+import torch
 
+import oracle
 import ring_parallelism_amd as ra
-from gpu_util import TOL, Problem, compare, expected_stats, say
+from gpu_util import DEV, TOL, Problem, compare, expected_stats, say, up
 
 pytestmark = pytest.mark.gpu
 
@@ -84,8 +86,6 @@ def _split_cases(n=40, seed=2025):
 def test_random_split_pass(case):
     """The block list cut into concurrent groups folded by the merge: the
     oracle's result over the visited blocks, and the single pass's counters."""
-    import torch
-    from gpu_util import DEV
     k = case
     say(f"random split pass {k}")
     p = Problem(k["S"], k["c"], k["split"], k["B"], k["h_q"], k["h_kv"], k["d"], "bf16", seed=k["seed"])
@@ -132,8 +132,6 @@ def test_random_natural_order_q_out(case):
     """Q read and out / lse written at global positions of natural-order
     tensors: the rank's rows equal its shard-layout result bit for bit, and
     no other row is touched."""
-    import torch
-    from gpu_util import DEV, up
     k = case
     say(f"random natural q/out {k}")
     p = Problem(k["S"], k["c"], k["split"], k["B"], k["h_q"], k["h_kv"], k["d"], k["dtype"], seed=k["seed"])
@@ -185,3 +183,92 @@ def test_random_decode_and_strided_merge(case):
     keys = np.concatenate([p.perm[t * p.n:(t + 1) * p.n] for t in k["blocks"]])
     ref_o, ref_l = p.ref(keys=keys)
     compare(out[:, :, None], lse[:, :, None], ref_o, ref_l, tol=TOL["bf16"])
+
+
+def _partition_cases(n=40, seed=2028):
+    g = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        split = SPLITS[int(g.integers(0, 3))]
+        c = int(g.integers(1, 17))
+        n_loc = int(g.integers(1, 400))
+        if split == ra.SPLIT_ZIGZAG and n_loc % 2:
+            n_loc += 1
+        out.append(dict(S=n_loc * c, c=c, split=split, outer=int(g.integers(1, 5)),
+                        inner=int(g.choice([1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 100, 256, 512])), seed=50_000 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _partition_cases(), ids=lambda k: f"S{k['S']}_c{k['c']}_sp{k['split']}_o{k['outer']}_b{k['inner']}")
+def test_random_partition_gather_scatter(case):
+    """Placement, gather and scatter at random sizes and row widths (any byte
+    count): perm and every byte against the oracle's partition."""
+    k = case
+    say(f"random partition {k}")
+    S, c, split, outer, inner = k["S"], k["c"], k["split"], k["outer"], k["inner"]
+    g = np.random.default_rng(k["seed"])
+    src = g.integers(0, 256, size=(outer, S, inner), dtype=np.uint8)
+    d_src = torch.from_numpy(src).to(DEV)
+    d_dst = torch.zeros((c, outer, S // c, inner), dtype=torch.uint8, device=DEV)
+    perm_d = torch.full((S,), -1, dtype=torch.int64, device=DEV)
+    ra.zigzag_partition(S, c, split, perm_d, d_src, d_dst, outer, inner)
+    perm = oracle.partition_perm(S, c, split)
+    back = torch.zeros_like(d_src)
+    ra.zigzag_unpartition(S, c, split, d_dst, back, outer, inner)
+    torch.cuda.synchronize()
+    assert np.array_equal(perm_d.cpu().numpy(), perm)
+    pr = perm.reshape(c, S // c)
+    assert np.array_equal(d_dst.cpu().numpy(), np.stack([src[:, pr[r]] for r in range(c)]))
+    assert np.array_equal(back.cpu().numpy(), src)
+
+
+def _merge_cases(n=30, seed=2029):
+    g = np.random.default_rng(seed)
+    dts = [ra.F32, ra.BF16]
+    out = []
+    for i in range(n):
+        pdt, odt = dts[int(g.integers(0, 2))], dts[int(g.integers(0, 2))]
+        out.append(dict(B=int(g.integers(1, 3)), H=int(g.integers(1, 5)), R=int(g.integers(1, 300)),
+                        d=int(g.choice([4, 8, 16, 32, 64, 128, 256])), n_parts=int(g.integers(1, 65)),
+                        parts_dtype=pdt, out_dtype=odt, in_place=bool(pdt == odt and g.random() < 0.3),
+                        seed=60_000 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _merge_cases(), ids=lambda k: f"B{k['B']}_H{k['H']}_R{k['R']}_d{k['d']}_n{k['n_parts']}"
+                                                             f"_p{k['parts_dtype']}_o{k['out_dtype']}{'_inplace' if k['in_place'] else ''}")
+def test_random_pointer_merge(case):
+    """ring_attn_merge with 1 .. 64 parts of random sizes and dtypes, in place
+    or not, with empty parts and empty rows, against the oracle's merge (of
+    the values the kernel reads)."""
+    k = case
+    say(f"random merge {k}")
+    g = np.random.default_rng(k["seed"])
+    B, H, R, d, n = k["B"], k["H"], k["R"], k["d"], k["n_parts"]
+    outs = g.standard_normal((n, B, H, R, d)).astype(np.float32)
+    lses = (g.standard_normal((n, B, H, R)) * 4).astype(np.float32)
+    empty = g.random((n, B, H, R)) < 0.1             # parts without keys for some rows
+    empty[:, 0, 0, 0] = True                         # one row with no keys anywhere
+    lses[empty] = -np.inf
+    outs[empty] = 0.0
+    tdt = torch.float32 if k["parts_dtype"] == ra.F32 else torch.bfloat16
+    d_outs = [torch.from_numpy(outs[j]).to(DEV).to(tdt) for j in range(n)]
+    d_lses = [torch.from_numpy(lses[j]).to(DEV) for j in range(n)]
+    seen = np.stack([x.float().cpu().numpy() for x in d_outs]).astype(np.float64)  # bf16-rounded parts
+    ref_o, ref_l = oracle.merge(list(seen), [lses[j].astype(np.float64) for j in range(n)])
+    odt = torch.float32 if k["out_dtype"] == ra.F32 else torch.bfloat16
+    if k["in_place"]:
+        out, lse = d_outs[0], d_lses[0]
+    else:
+        out = torch.full((B, H, R, d), float("nan"), dtype=odt, device=DEV)
+        lse = torch.full((B, H, R), float("nan"), dtype=torch.float32, device=DEV)
+    ra.ring_attn_merge(B, H, R, d, d_outs, k["parts_dtype"], d_lses, out, k["out_dtype"], lse)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    bound = 1e-5 + (np.abs(ref_o) * 2.0 ** -8 if k["out_dtype"] == ra.BF16 else 0.0)
+    assert np.all(np.abs(o - ref_o) <= bound)
+    l = lse.cpu().numpy()
+    assert np.array_equal(np.isneginf(l), np.isneginf(ref_l))
+    fin = np.isfinite(ref_l)
+    assert np.abs(l[fin] - ref_l[fin]).max() <= 1e-5 if fin.any() else True
+    assert np.all(o[0, 0, 0] == 0.0)
