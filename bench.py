@@ -340,6 +340,17 @@ def suite(args):
         st = stat(timed(torch, fwd(w, desc, 0, qs[0], ks, vs, out, lse), reps, sc))
         emit({"measurement": "shard_pass", "workload": w.name, "mode": mode, **st,
               "tflops": round(f0 / (st["median_ms"] / 1e3) / 1e12, 1)})
+    # Same launch on lower-entropy operands (a diagnostic of the power-limited
+    # clock, not a result): N(0, 0.1^2) and all-zero Q, K, V.
+    desc = ra.make_desc(w.seq_len, w.n_shards, w.split, w.batch, w.h_q, w.h_kv, w.head_dim, ra.BF16, ra.BF16,
+                        True, w.scale)
+    for label, f in (("operands N(0,0.1^2)", 0.1), ("operands all zero", 0.0)):
+        q2, k2, v2 = ((x.float() * f).to(torch.bfloat16) for x in (qs[0], ks, vs))
+        st = stat(timed(torch, fwd(w, desc, 0, q2, k2, v2, out, lse), reps))
+        tf = f0 / (st["median_ms"] / 1e3) / 1e12
+        emit({"measurement": "shard_pass", "workload": w.name, "mode": label, **st, "tflops": round(tf, 1),
+              "pct_of_nominal": round(100 * tf / PEAK_BF16_TFLOPS, 2)})
+        del q2, k2, v2
     del qs, ks, vs, scrub
 
     split_suite(torch, ra, dev, reps)
