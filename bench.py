@@ -113,7 +113,7 @@ def main():
                          "MFMA probe, per-shard balance (32k tokens), warm/cold and overlap on/off "
                          "(131k tokens), partial+merge and bidirectional passes (262k tokens), split-KV "
                          "decode, and every workload's GPU time beside the fp64 oracle's")
-    ap.add_argument("--reps", type=int, default=5, help="repetitions per timed launch in --suite")
+    ap.add_argument("--reps", type=int, default=10, help="timed repetitions per launch in --suite (after 3 warm-ups)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the ring: run with --gpus 1 (got {args.gpus}); "
@@ -253,11 +253,12 @@ def device_inputs(w, torch, dev, blocks_for=None):
     return qs, ks, vs
 
 
-def timed(torch, fn, reps, scrub=None):
-    """Per-launch milliseconds of fn() from HIP events on the current stream;
-    with `scrub` (a large device tensor) the caches are flushed by a full
-    write of it before every launch."""
-    fn()
+def timed(torch, fn, reps, scrub=None, warmup=3):
+    """Per-launch milliseconds of fn() from HIP events on the current stream,
+    after `warmup` untimed launches; with `scrub` (a large device tensor) the
+    caches are flushed by a full write of it before every launch."""
+    for _ in range(warmup):
+        fn()
     torch.cuda.synchronize()
     ms = []
     for _ in range(reps):
