@@ -92,6 +92,18 @@ typedef struct {
  * K and V blocks stay in shard layout (the blocks that travel the ring). */
 #define RA_FLAG_NATURAL_QO 2u
 
+/* stats (when not NULL) holds RA_STATS_EVENTS_LEN int64 instead of 4: slot 4
+ * counts the mid-pass raises of a row's softmax reference -- the online
+ * softmax rescaling its earlier partial sums because a later block holds a
+ * larger score ("Sequence Parallelism and Ring Attention Quiz", Q3 and Q7) --
+ * summed over rows, batch and heads; slot 5 the query tiles that were recomputed by the plain
+ * per-tile online softmax (an exponential left the fp32 range between two
+ * reference checks, or a row of the first tile sees no key).  Both depend on
+ * the data and on the tile order, not only on the shapes.  bf16 inputs; with
+ * fp32 inputs slots 4 and 5 stay 0. */
+#define RA_FLAG_EVENT_COUNTS 4u
+#define RA_STATS_EVENTS_LEN 6
+
 /* Shard placement and optional gather into shard-major order.
  *
  * perm (device int64[S], may be NULL): perm[r*(S/c) + t] = global position

@@ -19,6 +19,8 @@ F32 = 0
 BF16 = 1
 FLAG_SYNC_LOADS = 1
 FLAG_NATURAL_QO = 2
+FLAG_EVENT_COUNTS = 4
+STATS_EVENTS_LEN = 6
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 MAX_BLOCKS = 128
 MAX_PARTS = 64

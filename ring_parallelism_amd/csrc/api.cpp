@@ -60,7 +60,7 @@ ra_status check_desc(const ra_attn_desc* d) {
     return fail(RA_EUNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
   if (d->in_dtype == RA_F32 && d->out_dtype == RA_BF16)
     return fail(RA_EUNSUPPORTED, "fp32 inputs with bf16 output are not supported");
-  if ((d->flags & ~(RA_FLAG_SYNC_LOADS | RA_FLAG_NATURAL_QO)) != 0)
+  if ((d->flags & ~(RA_FLAG_SYNC_LOADS | RA_FLAG_NATURAL_QO | RA_FLAG_EVENT_COUNTS)) != 0)
     return fail(RA_EINVAL, "unknown flags 0x%x", d->flags);
   if ((d->flags & RA_FLAG_SYNC_LOADS) && d->in_dtype != RA_BF16)
     return fail(RA_EUNSUPPORTED, "RA_FLAG_SYNC_LOADS applies to bf16 inputs only");
@@ -184,6 +184,7 @@ static ra_status shard_params(const ra_attn_desc* desc, int32_t rank, const void
   p.scale_log2 = (float)((double)desc->scale * 1.4426950408889634);
   p.sync_loads = (desc->flags & RA_FLAG_SYNC_LOADS) ? 1 : 0;
   p.qo_natural = (desc->flags & RA_FLAG_NATURAL_QO) ? 1 : 0;
+  p.event_counts = (desc->flags & RA_FLAG_EVENT_COUNTS) ? 1 : 0;
   p.qo_rows = p.qo_natural ? desc->seq_len : p.n_loc;
   p.n_splits = 1;
   return RA_OK;

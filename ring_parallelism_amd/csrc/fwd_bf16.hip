@@ -6,20 +6,19 @@
 // parallelism" notes, section 4; "Sequence Parallelism and Ring Attention
 // Quiz", Q3 and Q7).  Blocks that would arrive over the ring are streamed
 // HBM -> LDS by the buffer unit's LDS-direct loads (no register staging)
-// into a six-stage ring, so that the tiles after the one being computed are
-// already in flight (the prefetch that hides the ring's transfers); a tile's
-// K fragments move on from LDS into registers one step before its score
-// products.  The
-// causal mask is resolved per (block, tile) from token positions:
-// tiles entirely after the query tile are never loaded, tiles entirely before
-// it run unmasked, and only tiles that straddle the diagonal (or the shard
-// end) apply an elementwise mask.
+// into a ring of LDS stages, so that the tiles after the one being computed
+// are already in flight (the prefetch that hides the ring's transfers); a
+// tile's K fragments move on from LDS into registers one step before its
+// score products.  The causal mask is resolved per (block, tile) from token
+// positions: tiles entirely after the query tile are never loaded, tiles
+// entirely before it run unmasked, and only tiles that straddle the diagonal
+// (or the shard end) apply an elementwise mask.
 //
 // Matrix-core formulation (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
 //   S^T = K Q^T    A = a 32-key slice of K (LDS, ds_read_b128), B = Q^T
 //                  (registers for the whole pass).  Each lane then owns one
-//                  query column and 16 of its scores, so a row max is an
-//                  in-lane max plus one permlane32 swap.
+//                  query column and 16 of its scores, so a row reduction is
+//                  in-lane plus one permlane32 swap.
 //   O^T += V^T P^T A = V^T, read from the row-major V tile with the
 //                  transposing LDS read (ds_read_b64_tr_b16); B = P^T taken
 //                  straight from the score registers after exp2 and a bf16
@@ -29,14 +28,19 @@
 // the ds_read_b128 of K and the transposing reads of V hit distinct banks.
 //
 // The softmax works in the log2 domain (scale * log2 e folded into one fma
-// before v_exp_f32) against a per-row reference m that is a real score max
-// but may trail the running max: any reference works as long as O and l
-// share it, so the result is the same up to rounding.  No per-tile row max is
-// taken.  The exponentials of a tile are summed anyway (for l); when a lane's
-// 16-term sum exceeds 2^16 -- some exponent above 16 -- the tile is redone
-// after raising m to its true max and rescaling O and l.  Exponents therefore
-// stay <= 16 (nothing can overflow), and the max, rescale and redo run on a
-// handful of tiles per row.
+// before v_exp_f32) against a per-row reference m.  Any reference gives the
+// same result as long as O and l share it (O / l and m + log2 l do not
+// depend on it), and nothing is lost by a reference below the running max as
+// long as no exponential overflows: fp32 and bf16 keep their relative
+// precision at every magnitude.  So the first tile sets m to its exact row
+// max and afterwards no per-tile max is taken.  At every workgroup barrier
+// (every G steps) a row whose lane sum l has passed 2^32 -- some scores rose
+// more than 32 log2 units above m -- raises m by the integer part of log2 l
+// and rescales O and l by that exact power of two.  Between two checks a
+// score would have to jump more than 96 log2 units above every earlier one
+// to overflow; if that happens (or a row of the first tile sees no key, as
+// some block orders allow), the query tile is recomputed from scratch by the
+// plain per-tile online softmax (exact tile max, rescale whenever it rises).
 //
 // Workgroup: NW wavefronts x NB 32-row blocks = BQ query rows of one
 // (batch, head).  Each workgroup takes query tiles p and n_qtiles-1-p of the
@@ -53,44 +57,55 @@
 #include "ra_common.h"
 #include "tile_common.h"
 
-// Tile configuration: waves per workgroup, 32-row query blocks per wave,
-// 32-key blocks per pipeline step.  (Compile-time knobs for tuning sweeps.)
+// Tile configuration: waves per workgroup, LDS ring stages, steps per
+// workgroup barrier.  (Compile-time knobs for tuning sweeps.)
 #ifndef RA_FWD_NW
 #define RA_FWD_NW 8
 #endif
-#ifndef RA_FWD_NB
-#define RA_FWD_NB 1
-#endif
-#ifndef RA_FWD_MB
-#define RA_FWD_MB 1
-#endif
 #ifndef RA_FWD_STAGES
-#define RA_FWD_STAGES 6
+#define RA_FWD_STAGES 8
 #endif
-#ifndef RA_FWD_PAIRED
-#define RA_FWD_PAIRED 1
+#ifndef RA_FWD_GROUP
+#define RA_FWD_GROUP 2
+#endif
+#ifndef RA_FWD_WPE
+#define RA_FWD_WPE 1
 #endif
 
 namespace ra {
 namespace {
 
-// Largest 16-term in-lane sum of exponentials accepted without raising the
-// reference (each term is then <= 2^16).
-constexpr float kSumLimit = 65536.0f;
+// A row's lane sum l above this raises the reference (at a barrier).
+constexpr float kRaiseAt = 4294967296.0f;  // 2^32
+#ifndef RA_FWD_PINP
+#define RA_FWD_PINP 0
+#endif
+constexpr bool kPinP = RA_FWD_PINP != 0;
 
-template <int D, int NW, int NB, int MB>
+constexpr int gcd2(int a, int b) { return b == 0 ? a : gcd2(b, a % b); }
+constexpr int lcm3(int a, int b, int c) {
+  const int ab = a / gcd2(a, b) * b;
+  return ab / gcd2(ab, c) * c;
+}
+
+template <int D, int NW, int NB>
 struct Cfg {
   static constexpr int NT = NW * 64;
   static constexpr int BQ = NW * NB * 32;
-  static constexpr int BK = MB * 32;                  // keys per tile (MB 32-key MFMA blocks)
+  static constexpr int BK = 32;                       // keys per tile (one 32-key MFMA block)
   static constexpr int ROWB = D * 2;                  // bytes per K / V row
   static constexpr int CHUNKS = ROWB / 16;            // 16-byte chunks per row
   static constexpr int TILEB = BK * ROWB;             // bytes per K or V tile
-  static constexpr int STAGES = RA_FWD_STAGES;  // LDS ring depth (4..6)
-  static_assert(STAGES >= 4 && STAGES <= 6, "stages");
-  // One barrier per two steps (loads issued two tiles at a time); needs 6 stages.
-  static constexpr bool PAIRED = RA_FWD_PAIRED != 0;
-  static_assert(!PAIRED || STAGES == 6, "paired steps use six stages");
+  static constexpr int STAGES = RA_FWD_STAGES;        // LDS ring depth
+  static constexpr int G = RA_FWD_GROUP;              // steps per barrier (loads issued G tiles at a time)
+  static constexpr int AHEAD = STAGES - G;            // tiles in flight before a group's loads
+  // The K fragments of tile i+2 are read during step i, so that tile must
+  // have been published by the barrier of an earlier group: AHEAD >= G + 2.
+  static_assert(AHEAD >= G + 2 && G >= 1 && G <= 4, "stage / group configuration");
+  // Tiles of a group's loads that the next group does not read yet (they may
+  // stay in flight across its closing barrier), and the matching vmcnt.
+  static constexpr int LATE = (AHEAD - G - 2) < G ? (AHEAD - G - 2) : G;
+  static_assert(STAGES * TILEB <= 65536, "stage offsets must fit the 16-bit LDS immediate");
   static constexpr int RPI = 1024 / ROWB;             // rows per 64-lane 16-byte load
   static constexpr int LOADS = TILEB / 1024 / NW;     // loads per wave per tile, each tensor
   static_assert(LOADS >= 1 && TILEB % (1024 * NW) == 0, "tile must split evenly over waves");
@@ -100,34 +115,41 @@ struct Cfg {
   __device__ static int v_slot(int r, int c) { return Swizzle<D>::v_slot(r, c); }
 };
 
-template <int D, int NW, int NB, int MB, typename OutT>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
-  using C = Cfg<D, NW, NB, MB>;
+template <int D, int NW, int NB, typename OutT>
+__global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams p) {
+  using C = Cfg<D, NW, NB>;
   constexpr int kBK = C::BK;
-  // One LDS array: the K tiles of the STAGES ring stages, then their V tiles.
-  // Every LDS read of the tile loop is inline assembly with the stage offset
-  // as the instruction's immediate, so per-lane addresses are computed once.
-  // (The compiler cannot tell which stage an LDS-direct load fills, and would
-  // make compiler-visible reads wait for all loads in flight.)
-  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGES * C::TILEB];
+  constexpr int NS = C::STAGES;
+  constexpr int G = C::G;
+  // One LDS array: the K tiles of the ring stages, then their V tiles.  Every
+  // LDS read of the tile loop is inline assembly with the stage offset as the
+  // instruction's immediate, so per-lane addresses are computed once.  (The
+  // compiler cannot tell which stage an LDS-direct load fills, and would make
+  // compiler-visible reads wait for all loads in flight.)
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NS * C::TILEB];
+  // Per query tile of the workgroup: 1 = recompute it by the exact path.
+  __shared__ int redo_flag[2];
   auto k_tile = [&](auto S) -> lds_char* { return (lds_char*)smem + decltype(S)::value * C::TILEB; };
   auto v_tile = [&](auto S) -> lds_char* {
-    return (lds_char*)smem + (C::STAGES + decltype(S)::value) * C::TILEB;
+    return (lds_char*)smem + (NS + decltype(S)::value) * C::TILEB;
   };
-  static_assert(C::STAGES * C::TILEB <= 65536, "stage offsets must fit the 16-bit LDS immediate");
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int lc = lane & 31;  // query column inside a 32-block
   const int g = lane >> 5;   // half-wave
+  if (tid == 0) {
+    redo_flag[0] = 0;
+    redo_flag[1] = 0;
+  }
 
   // XCD-aware work decode: hardware deals workgroup ids round-robin over the
   // 8 XCDs, so id -> (id % 8) * (G / 8) + id / 8 keeps consecutive logical
   // items on one XCD.
-  const int G = gridDim.x;
+  const int n_wg = gridDim.x;
   const int bid = blockIdx.x;
-  const int wl_all = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  const int wl_all = (n_wg % 8 == 0) ? (bid % 8) * (n_wg / 8) + bid / 8 : bid;
   // Split of the block list (one group when n_splits = 1): this workgroup
   // folds blocks [t0, t1) and writes its own partial result.
   const int split = wl_all / p.grid_per_split;
@@ -164,7 +186,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
   const int v_d = 16 * (qg & 1) + 4 * (jj & 3);  // + 32 * d-block
 
   // LDS addresses of this lane's reads in stage 0 (other stages: + immediate).
-  static_assert(MB == 1, "one 32-key block per step");
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
   uint32_t kaddr[D / 16];  // K: key row lc, 16-byte chunk 2s+g
 #pragma unroll
@@ -173,10 +194,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
     const int d = db * 32 + v_d;
-    vaddr[db] = lds0 + C::STAGES * C::TILEB + v_row * C::ROWB + C::v_slot(v_row, d >> 3) * 16 + (d & 7) * 2;
+    vaddr[db] = lds0 + NS * C::TILEB + v_row * C::ROWB + C::v_slot(v_row, d >> 3) * 16 + (d & 7) * 2;
   }
 
   uint32_t pairs_partial = 0;  // per lane, masked tiles only
+  uint32_t n_raise = 0;        // per lane (g == 0 counts its row): mid-pass reference raises
+  uint32_t n_exact = 0;        // query tiles recomputed by the exact path (workgroup-uniform)
 
   const int n_q = (p.n_qtiles - 1 - pair != pair) ? 2 : 1;
 
@@ -204,19 +227,23 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
     }
 
     f32x16 oacc[D / 32][NB];
+    float m_ref[NB], l_part[NB], neg_sub[NB];
+    auto reset_state = [&]() {
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) oacc[db][nb] = f32x16{};
-    float m_ref[NB], l_part[NB];
+        for (int nb = 0; nb < NB; ++nb) oacc[db][nb] = f32x16{};
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      m_ref[nb] = -INFINITY;
-      l_part[nb] = 0.f;
-    }
+      for (int nb = 0; nb < NB; ++nb) {
+        m_ref[nb] = -INFINITY;
+        l_part[nb] = 0.f;
+        neg_sub[nb] = 0.f;  // -m_ref, or 0 while m_ref is -inf
+      }
+    };
+    reset_state();
 
     // Tile iterator over (block t, key tile kt), skipping blocks with no
-    // visible key.  A state is (t, kt, n_vis, n_full); t >= n_blocks: done.
+    // visible key.  A state is (t, kt, n_vis, n_full); t >= t1: done.
     // The cursor also carries the block's K and V base addresses, read from
     // the argument block once per block: a scalar load in the per-tile path
     // would make every tile wait for all of the wave's LDS reads as well.
@@ -244,10 +271,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       }
       return x;
     };
-    auto valid = [&](const Tile& x) { return x.t < t1; };
 
-    // Put tile x's K and V into LDS stage `st`.  Rows past the shard end fall
-    // outside the buffer resource and read as zeros.
+    // Put tile x's K and V into LDS stage `st`.  The tile offset is part of
+    // each lane's offset, so the buffer range check covers it: rows past the
+    // shard end fall outside the (batch, kv head) slice and read as zeros.
     auto issue_loads = [&](auto S, const Tile& x) {
       const __amdgpu_buffer_rsrc_t rk =
           __builtin_amdgcn_make_buffer_rsrc((void*)x.kb, (short)0, kv_bytes, kRsrcWord3);
@@ -257,21 +284,21 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int u = 0; u < C::LOADS; ++u) {
         const int grp = wave * C::LOADS + u;  // 1 KiB group of the tile
-        lds_load16(rk, k_tile(S) + grp * 1024, ld_koff[u], tile_off);
-        lds_load16(rv, v_tile(S) + grp * 1024, ld_voff[u], tile_off);
+        lds_load16(rk, k_tile(S) + grp * 1024, ld_koff[u] + tile_off, 0);
+        lds_load16(rv, v_tile(S) + grp * 1024, ld_voff[u] + tile_off, 0);
       }
     };
 
     // S^T = K Q^T for the tile in stage S: D/16 16-wide slices of d, up to
-    // six K reads in flight ahead of the products (measured best of 2..8 at
-    // d = 128; lgkmcnt counts LDS reads in issue order, and the wait before
-    // slice s allows the reads issued after it).
-    auto qk = [&](f32x16 (&sacc)[MB][NB], auto S) {
+    // six K reads in flight ahead of the products (lgkmcnt counts LDS reads
+    // in issue order, and the wait before slice s allows the reads issued
+    // after it).  Used where no other LDS read is in flight.
+    auto qk = [&](f32x16 (&sacc)[NB], auto S) {
       constexpr int OFF = decltype(S)::value * C::TILEB;
       constexpr int NR = D / 16, PF = NR < 6 ? NR : 6;
       bf16x8 a[NR];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sacc[0][nb] = f32x16{};
+      for (int nb = 0; nb < NB; ++nb) sacc[nb] = f32x16{};
       // (Explicit captures: clang does not capture variables that a generic
       // lambda uses only as inline-assembly operands.)
       static_for<0, PF>([&a, &kaddr](auto I) {
@@ -285,15 +312,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
         asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a[sl]) : "n"(issued - sl - 1));
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          sacc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[sl], qreg[nb][sl], sacc[0][nb], 0, 0, 0);
+          sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[sl], qreg[nb][sl], sacc[nb], 0, 0, 0);
       });
     };
 
     // Elementwise mask on a tile that straddles the diagonal or the shard
-    // end.  Key positions ascend inside a block, so the keys a query sees
-    // there are the block's first count_upto(j, pos_q) rows: one bound per
-    // row.  Accumulator element i of block mb is key mb*32 + (i/4)*8 + g*4 + i%4.
-    auto mask = [&](f32x16 (&sacc)[MB][NB], const Tile& x) {
+    // end (works on raw or shifted scores alike).  Key positions ascend inside
+    // a block, so the keys a query sees there are the block's first
+    // count_upto(j, pos_q) rows: one bound per row.  Accumulator element i is
+    // key (i/4)*8 + g*4 + i%4 of the tile.
+    auto mask = [&](f32x16 (&sacc)[NB], const Tile& x) {
       const int j = p.owner[x.t];
       int lim[NB];
 #pragma unroll
@@ -303,118 +331,82 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
         lim[nb] = cnt - x.kt * kBK - g * 4;
       }
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int i = 0; i < 16; ++i) {
+        const int off = (i / 4) * 8 + (i % 4);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int off = mb * 32 + (i / 4) * 8 + (i % 4);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const bool vis = off < lim[nb];
-            pairs_partial += vis ? 1u : 0u;
-            sacc[mb][nb][i] = vis ? sacc[mb][nb][i] : -INFINITY;
-          }
+        for (int nb = 0; nb < NB; ++nb) {
+          const bool vis = off < lim[nb];
+          pairs_partial += vis ? 1u : 0u;
+          sacc[nb][i] = vis ? sacc[nb][i] : -INFINITY;
         }
+      }
     };
 
     // Tile max of the scaled scores (log2 units), both half-waves combined.
-    auto row_max = [&](const f32x16 (&sacc)[MB][NB], float (&mt)[NB]) {
+    auto row_max = [&](const f32x16 (&sacc)[NB], float (&mt)[NB]) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         float mx = -INFINITY;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mb][nb][i]);
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[nb][i]);
         mt[nb] = halves_max(mx) * p.scale_log2;
       }
     };
 
-    // Tile max in absolute log2 units of x values already shifted by the
-    // reference (x = scale*log2(e)*s - m_ref; m_ref = -inf: shifted by 0).
-    auto xmax = [&](const f32x16 (&x)[MB][NB], float (&mt)[NB]) {
+    // x = scale*log2(e)*s - m_ref, in place (m_ref = -inf: shifted by 0).
+    auto shift = [&](f32x16 (&sacc)[NB]) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        float mx = -INFINITY;
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x[mb][nb][i]);
-        mt[nb] = halves_max(mx) + ((m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb]);
-      }
-    };
-
-    // x = scale*log2(e)*s - m_ref, in place (m_ref = -inf: shift by 0).
-    auto shift = [&](f32x16 (&sacc)[MB][NB]) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const float msub = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sacc[mb][nb][i] = __builtin_fmaf(sacc[mb][nb][i], p.scale_log2, -msub);
-      }
+        for (int i = 0; i < 16; ++i) sacc[nb][i] = __builtin_fmaf(sacc[nb][i], p.scale_log2, neg_sub[nb]);
     };
 
     // Raise the reference to the tile max mt (absolute, log2 units) where it
     // is higher: rescale O and l, and re-shift the tile's x values.
-    auto rescale = [&](const float (&mt)[NB], f32x16 (&xnext)[MB][NB]) {
+    auto rescale = [&](const float (&mt)[NB], f32x16 (&xs)[NB]) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const float m_new = fmaxf(m_ref[nb], mt[nb]);
         const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref[nb] - m_new);
-        const float old_sub = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
-        const float new_sub = (m_new == -INFINITY) ? 0.f : m_new;
-        const float dx = old_sub - new_sub;
+        const float new_neg = (m_new == -INFINITY) ? 0.f : -m_new;
+        const float dx = new_neg - neg_sub[nb];
         l_part[nb] *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) oacc[db][nb] *= alpha;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) xnext[mb][nb][i] += dx;
+        for (int i = 0; i < 16; ++i) xs[nb][i] += dx;
         m_ref[nb] = m_new;
+        neg_sub[nb] = new_neg;
       }
     };
 
     // P = bf16(exp2(x)) as the B operand of the value product; ls gets the
     // lane's fp32 sum of the tile (the log-sum-exp needs it unrounded).
-    auto exps = [&](const f32x16 (&x)[MB][NB], bf16x8 (&pb)[NB][2 * MB], float (&ls)[NB]) {
+    auto exps = [&](const f32x16 (&x)[NB], bf16x8 (&pb)[NB][2], float (&ls)[NB]) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         float sum = 0.f;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int hh = 0; hh < 2; ++hh) {
+          bf16x8 v8;
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            bf16x8 v8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float pe = __builtin_amdgcn_exp2f(x[mb][nb][hh * 8 + e]);
-              sum = (mb == 0 && hh == 0 && e == 0) ? pe : sum + pe;
-              v8[e] = (__bf16)pe;
-            }
-            pb[nb][mb * 2 + hh] = v8;
+          for (int e = 0; e < 8; ++e) {
+            const float pe = __builtin_amdgcn_exp2f(x[nb][hh * 8 + e]);
+            sum = (hh == 0 && e == 0) ? pe : sum + pe;
+            v8[e] = (__bf16)pe;
           }
+          pb[nb][hh] = v8;
+        }
         ls[nb] = sum;
       }
     };
 
-    // Rows whose reference is still unset (no visible key folded yet) take
-    // the max-based path on every tile until they get one.
-    auto any_unset = [&]() {
-      bool u = false;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) u |= m_ref[nb] == -INFINITY && posq[nb] >= 0;
-      return __builtin_amdgcn_ballot_w64(u) != 0;
-    };
-
     // The transposing reads of the V tile in stage S (for each 32-wide slice
-    // of d, two 16-key halves of 8 rows each), issued a block of work ahead
-    // of the value product so that their latency is hidden.
-    auto v_reads = [&vaddr](auto S, bf16x8 (&va)[D / 32][2 * MB]) {
+    // of d, two 16-key halves of 8 rows each).
+    auto v_reads = [&vaddr](auto S, bf16x8 (&va)[D / 32][2]) {
       constexpr int OFF = decltype(S)::value * C::TILEB;
       static_for<0, D / 32>([&vaddr, &va](auto DB) {
-        static_for<0, 2 * MB>([&vaddr, &va](auto K16) {
+        static_for<0, 2>([&vaddr, &va](auto K16) {
           constexpr int db = decltype(DB)::value, k16 = decltype(K16)::value;
           constexpr int o = OFF + k16 * 16 * C::ROWB;
           bf16x4 lo, hi;
@@ -425,11 +417,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       });
     };
 
-    // O^T += V^T P^T, 16 keys per MFMA step, from the reads above (no other
-    // LDS read is issued in between: the wait before slice db lets the
-    // reads of the later slices stay in flight).
-    auto pv = [&](bf16x8 (&va)[D / 32][2 * MB], const bf16x8 (&pb)[NB][2 * MB]) {
-      static_assert(MB == 1, "one 32-key block per step");
+    // O^T += V^T P^T, 16 keys per MFMA step, straight after v_reads (no
+    // other LDS read in between: the wait before slice db lets the reads of
+    // the later slices stay in flight).
+    auto pv = [&](bf16x8 (&va)[D / 32][2], const bf16x8 (&pb)[NB][2]) {
       static_for<0, D / 32>([&va, &pb, this_oacc = &oacc](auto DB) {
         auto& oacc = *this_oacc;
         constexpr int db = decltype(DB)::value;
@@ -442,11 +433,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       });
     };
 
-    // With paired steps the K fragments of tile i+2 are read into registers
-    // during the value product of step i (that tile landed before the barrier
-    // closing step i-1): the score products of step i+1 then start without an
-    // LDS wait, and a step's LDS reads split between its halves -- V beside
-    // the score products, K beside the value product.
+    // The K fragments of tile i+2 are read into registers during the value
+    // product of step i (that tile was published by an earlier barrier): the
+    // score products of step i+1 then start without an LDS wait, and a
+    // step's LDS reads split between its halves -- V beside the score
+    // products, K beside the value product.
     auto k_reads = [&kaddr](auto S, bf16x8 (&kf)[D / 16]) {
       constexpr int OFF = decltype(S)::value * C::TILEB;
       static_for<0, D / 16>([&kaddr, &kf](auto I) {
@@ -454,23 +445,22 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       });
     };
     // S^T = K Q^T from fragments read by k_reads a step earlier (the last LDS
-    // reads issued): one wait for all of them, so that the V reads issued next
-    // are not held behind per-slice waits.
-    auto qk_held = [&](f32x16 (&sacc)[MB][NB], bf16x8 (&kf)[D / 16]) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sacc[0][nb] = f32x16{};
+    // reads issued): one wait for all of them.
+    auto qk_held = [&](f32x16 (&sacc)[NB], bf16x8 (&kf)[D / 16]) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
       for (int sl = 0; sl < D / 16; ++sl) asm volatile("" : "+v"(kf[sl]));
 #pragma unroll
-      for (int sl = 0; sl < D / 16; ++sl)
+      for (int nb = 0; nb < NB; ++nb) {
+        sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qreg[nb][0], f32x16{}, 0, 0, 0);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          sacc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sl], qreg[nb][sl], sacc[0][nb], 0, 0, 0);
+        for (int sl = 1; sl < D / 16; ++sl)
+          sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sl], qreg[nb][sl], sacc[nb], 0, 0, 0);
+      }
     };
-    // O^T += V^T P^T from V reads the caller has waited for (same order of
-    // products per accumulator as pv).
-    auto pv_held = [&](bf16x8 (&va)[D / 32][2 * MB], const bf16x8 (&pb)[NB][2 * MB]) {
+    // O^T += V^T P^T from V reads the caller has waited for, key half 0
+    // first (it needs only the first eight exponentials of each lane).
+    auto pv_held = [&](bf16x8 (&va)[D / 32][2], const bf16x8 (&pb)[NB][2]) {
 #pragma unroll
       for (int k16 = 0; k16 < 2; ++k16)
 #pragma unroll
@@ -480,15 +470,70 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
             oacc[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][k16], pb[nb][k16], oacc[db][nb], 0, 0, 0);
     };
 
-    // Software pipeline over the tile sequence, C::STAGES LDS stages in a
-    // ring.  Step i: the scores of tile i+1 run on the matrix cores beside
-    // the exponentials of tile i on the vector unit; then the value product
-    // of tile i runs beside the shift of tile i+1 (and, with paired steps,
-    // the K reads of tile i+2).  Loads run STAGES-2 tiles ahead: with paired
-    // steps, every even step issues two tiles and every odd step ends with the
-    // workgroup barrier; otherwise one tile and one barrier per step.  Two cursors walk the tile list: `ld` (the tile being
-    // loaded) and `nx` (tile i+1); n_tiles bounds both.
-    constexpr int NS = C::STAGES;
+    // Raise the reference of every row whose lane sum l has passed 2^32 by
+    // the integer part of log2 l (the same in both lanes of a row), with O and
+    // l rescaled by that exact power of two; a non-finite l marks the query
+    // tile for the exact path.
+    // y (the shifted scores of the next tile) moves with the reference.
+    auto raise_ref = [&](bool& bad, f32x16 (&ys)[NB]) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const float lr = halves_max(l_part[nb]);
+        const bool fin = lr < INFINITY;
+        bad |= !fin;
+        const int e = __builtin_amdgcn_frexp_expf(lr);  // lr = f * 2^e, f in [0.5, 1)
+        const int dd = (fin && lr > kRaiseAt) ? e - 1 : 0;
+        n_raise += (dd != 0 && g == 0) ? 1u : 0u;
+        l_part[nb] = __builtin_ldexpf(l_part[nb], -dd);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int e2 = 0; e2 < 16; ++e2) oacc[db][nb][e2] = __builtin_ldexpf(oacc[db][nb][e2], -dd);
+#pragma unroll
+        for (int e2 = 0; e2 < 16; ++e2) ys[nb][e2] -= (float)dd;
+        m_ref[nb] += (float)dd;
+        neg_sub[nb] -= (float)dd;
+      }
+    };
+
+    // The plain online softmax over every visible tile, one tile at a time
+    // through LDS stage 0: exact tile max, rescale of O and l whenever it
+    // rises.  Recomputes the query tile from scratch.
+    f32x16 xa[NB], xb[NB];
+    bf16x8 pb[NB][2], va[D / 32][2];
+    float mt[NB], ls[NB];
+    const uint32_t pairs_before = pairs_partial;
+    auto exact_pass = [&]() {
+      pairs_partial = pairs_before;
+      ++n_exact;
+      reset_state();
+      for (int t = t0; t < t1; ++t) {
+        Tile x;
+        x.t = t;
+        x.kt = 0;
+        block_counts(x);
+        for (int kt = 0; kt < x.vis; ++kt) {
+          x.kt = kt;
+          __syncthreads();  // every wave has finished reading stage 0
+          issue_loads(Ic<0>{}, x);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          qk(xa, Ic<0>{});
+          if (kt >= x.full) mask(xa, x);
+          row_max(xa, mt);
+          shift(xa);
+          rescale(mt, xa);
+          exps(xa, pb, ls);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) l_part[nb] += ls[nb];
+          v_reads(Ic<0>{}, va);
+          pv(va, pb);
+        }
+      }
+      __syncthreads();
+    };
+
+    // The first tile: loads of tiles 0 .. AHEAD-1, its scores, exact row max.
     Tile first;
     first.t = -1;
     first.kt = 0;
@@ -499,143 +544,134 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
     for (int t = t0; t < t1; ++t) {
       Tile x;
       x.t = t;
+      x.kt = 0;
       block_counts(x);
       if (x.vis > 0 && first.t < 0) first = x;
       n_tiles += x.vis;
     }
-    Tile ld = first, nx = first;
-    if (n_tiles > 0) issue_loads(Ic<0>{}, ld);
-    ld = advance(ld);
-    nx = ld;
-    if (n_tiles > 1) issue_loads(Ic<1>{}, ld);
-    ld = advance(ld);
-    if (n_tiles > 2) issue_loads(Ic<2>{}, ld);
-    ld = advance(ld);
-    if constexpr (NS > 4) {
-      if (n_tiles > 3) issue_loads(Ic<3>{}, ld);
-      ld = advance(ld);
-    }
-    if constexpr (NS > 5 && !C::PAIRED) {
-      if (n_tiles > 4) issue_loads(Ic<4>{}, ld);
-      ld = advance(ld);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    // Every row of the query tile sees key 0 of the first tile (so that the
+    // first tile gives every row a finite reference) unless a causal mask
+    // hides it from the tile's first row (positions ascend).
+    const bool fast = n_tiles > 0 &&
+                      (!p.causal || count_upto32(p.owner[first.t], pos_first, n_loc, p.c, p.split) >= 1);
+    if (fast) {
+      Tile ld = first;
+      static_for<0, C::AHEAD>([&](auto I) {
+        if (decltype(I)::value < n_tiles) issue_loads(I, ld);
+        ld = advance(ld);
+      });
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
 
-    f32x16 xa[MB][NB], xb[MB][NB];
-    bf16x8 pb[NB][2 * MB], va[D / 32][2 * MB];
-    float mt[NB], ls[NB];
-    bool unset = false;
-    bf16x8 kf[D / 16];  // K fragments of the next tile (paired steps)
-    if (n_tiles > 0) {
+      bf16x8 kf[D / 16];  // K fragments of the next tile
       qk(xa, Ic<0>{});
-      if constexpr (C::PAIRED) k_reads(Ic<1>{}, kf);
+      k_reads(Ic<1>{}, kf);
       if (first.kt >= first.full) mask(xa, first);
       row_max(xa, mt);
       shift(xa);
-      rescale(mt, xa);  // first reference max (O and l are still zero)
-      unset = any_unset();
-    }
+      rescale(mt, xa);  // first reference: the exact max (O and l are still zero)
+      bool bad = false;
 
-    // Step i at compile-time rotation position K: tiles i, i+1 and i+NS-1
-    // live in stages K, K+1 and K+NS-1 (mod NS); the score buffers swap each
-    // step.  Returns false once tile i+1 is past the end.
-    int i = 0;
-    auto step = [&](auto K) {
-      constexpr int k = decltype(K)::value;
-      auto& x = (k % 2 == 0) ? xa : xb;
-      auto& y = (k % 2 == 0) ? xb : xa;
-      const bool has_next = i + 1 < n_tiles;
-      if constexpr (!C::PAIRED) {
-        if (i + NS - 1 < n_tiles) issue_loads(Ic<(k + NS - 1) % NS>{}, ld);
-        ld = advance(ld);
-      } else if constexpr (k % 2 == 0) {
-        // Paired steps: tiles i+4 and i+5 refill the stages of tiles i-2 and
-        // i-1, released by the barrier that closed step i-1.
-        if (i + 4 < n_tiles) issue_loads(Ic<(k + 4) % NS>{}, ld);
-        ld = advance(ld);
-        if (i + 5 < n_tiles) issue_loads(Ic<(k + 5) % NS>{}, ld);
-        ld = advance(ld);
-        // Measurement mode: no overlap of the tile transfers with compute.
-        if (p.sync_loads) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-      // Scores of tile i+1 (harmless when there is no tile i+1).
-      if constexpr (C::PAIRED) {
-        qk_held(y, kf);
-      } else {
-        qk(y, Ic<(k + 1) % NS>{});
-      }
-      v_reads(Ic<k % NS>{}, va);
-      exps(x, pb, ls);
-      bool over = false;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) over |= ls[nb] > kSumLimit;
-      if ((__builtin_amdgcn_ballot_w64(over) != 0) | unset) {
-        // Rare path (a real branch: if-converting it would put the output
-        // rescale on every tile): raise the reference to tile i's max and
-        // redo its exponentials.
-        asm volatile("" ::: "memory");
-        xmax(x, mt);
-        rescale(mt, x);
+      // Step i at compile-time rotation position K: tiles i, i+1 and i+2 live
+      // in stages K, K+1 and K+2 (mod NS); x holds tile i's shifted scores
+      // (masked), y receives tile i+1's.  Control flow (mask, loads, barrier,
+      // reference check) sits at the step boundaries only, so the body is one
+      // straight-line block for the scheduler.  Returns false after the last
+      // tile.
+      int i = 0;
+      Tile nx = advance(first);  // tile i+1
+      auto step = [&](auto K) {
+        constexpr int k = decltype(K)::value;
+        auto& x = (k % 2 == 0) ? xa : xb;
+        auto& y = (k % 2 == 0) ? xb : xa;
+        if constexpr (k % G == 0) {
+          // Tiles i+AHEAD .. i+AHEAD+G-1 refill the stages of tiles i-G ..
+          // i-1, released by the barrier that closed step i-1.
+          static_for<0, G>([&](auto J) {
+            constexpr int jx = decltype(J)::value;
+            if (i + C::AHEAD + jx < n_tiles) issue_loads(Ic<(k + C::AHEAD + jx) % NS>{}, ld);
+            ld = advance(ld);
+          });
+          // Measurement mode: no overlap of the tile transfers with compute.
+          if (p.sync_loads) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        // ---- straight-line body ----
+        qk_held(y, kf);  // scores of tile i+1 (harmless past the end)
+        v_reads(Ic<k % NS>{}, va);
         exps(x, pb, ls);
-        unset = any_unset();
-      }
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) l_part[nb] += ls[nb];
-      // Materialise P here, beside the score products.
+        for (int nb = 0; nb < NB; ++nb) l_part[nb] += ls[nb];
+        if constexpr (kPinP) {
+          // P is complete beside the score products: the vector work of the
+          // exponentials stays in the first half of the step.
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int k4 = 0; k4 < 2 * MB; ++k4) asm volatile("" : "+v"(pb[nb][k4]));
-      if (has_next && nx.kt >= nx.full) mask(y, nx);
-      if constexpr (C::PAIRED) {
+          for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+v"(pb[nb][0]), "+v"(pb[nb][1]));
+          __builtin_amdgcn_sched_barrier(0);
+        }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the V reads of tile i
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) asm volatile("" : "+v"(va[db][0]), "+v"(va[db][1]));
         k_reads(Ic<(k + 2) % NS>{}, kf);  // tile i+2 (harmless past the end)
         pv_held(va, pb);
-      } else {
-        pv(va, pb);
-      }
-      shift(y);
-      // Keep the shift beside the value product (left alone, it sinks into
-      // the next step, where the vector unit already has the exponentials).
+        shift(y);
+        if constexpr (kPinP) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+v"(y[mb][nb]));
-      if constexpr (!C::PAIRED) {
-        // Tile i+2 must have landed before the next step reads it; the loads
-        // of tiles i+3 .. i+NS-1 may stay in flight.  Stage K must be drained
-        // before a later step refills it.
-        if (i + NS - 1 < n_tiles) {
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 3) * 2 * C::LOADS) : "memory");
-        } else {
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+v"(y[nb]));
         }
-        __syncthreads();
-      } else if constexpr (k % 2 == 1) {
-        // The tiles loaded at step i-1 are read from step i+2 on.
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        // ---- step boundary ----
+        if constexpr (k % G == G - 1) {
+          // The tiles the next group reads must have landed; the last LATE
+          // tiles loaded at the start of this group may stay in flight.
+          // A bare s_barrier: a fenced one would wait for every load in
+          // flight.  Every LDS read of a stage the next group refills was
+          // awaited inside its step.
+          if constexpr (C::LATE > 0) {
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::LATE * 2 * C::LOADS) : "memory");
+          } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          }
+          __builtin_amdgcn_s_barrier();
+          // Reference check (wave-uniform branch, rarely taken).
+          bool high = false;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) high |= l_part[nb] > kRaiseAt;
+          if (__builtin_amdgcn_ballot_w64(high) != 0) raise_ref(bad, y);
+        }
+        if (++i >= n_tiles) return false;
+        if (nx.kt >= nx.full) mask(y, nx);  // tile i (the next step's x)
+        nx = advance(nx);
+        return true;
+      };
+      // Stages rotate with period NS, the score buffers with period 2 and
+      // the load groups with period G.
+      constexpr int kUnroll = lcm3(NS, 2, G);
+      while (i < n_tiles) {
+        if (!unrolled_steps<0, kUnroll>(step)) break;
       }
-      nx = advance(nx);
-      return ++i < n_tiles;
-    };
-    // Stages rotate with period NS and the score buffers with period 2.
-    constexpr int kUnroll = NS % 2 == 0 ? NS : 2 * NS;
-    while (i < n_tiles) {
-      if (!unrolled_steps<0, kUnroll>(step)) break;
-    }
-    if constexpr (C::PAIRED) {
       // The last K reads issued ahead are never consumed: wait for them while
       // their registers are still reserved.
       static_for<0, D / 16>([&kf](auto I) { asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kf[I])); });
-    }
-    if constexpr (C::PAIRED) {
-      // A final barrier: the sequence may end between the paired barriers.
+      // A final barrier: the sequence may end between the group barriers.
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
+
+      // A row whose sum or output is not finite took an exponential past the
+      // fp32 range: recompute the query tile by the exact path.
+      float z = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        z = __builtin_fmaf(l_part[nb], 0.f, z);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int e2 = 0; e2 < 16; ++e2) z = __builtin_fmaf(oacc[db][nb][e2], 0.f, z);
+      }
+      bad |= !(z == 0.f);  // inf * 0 and NaN * 0 are NaN
+      if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) redo_flag[qi] = 1;
+      __syncthreads();
+      if (redo_flag[qi]) exact_pass();
+    } else if (n_tiles > 0) {
+      exact_pass();
     }
 
     // Epilogue: out = O / l, lse = ln 2 * (m_ref + log2 l).
@@ -700,6 +736,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
     if (lane == 0 && v) atomicAdd(p.stats + 0, v);
+    if (p.event_counts) {
+      unsigned long long r = n_raise;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) r += __shfl_xor(r, off);
+      if (lane == 0 && r) atomicAdd(p.stats + 4, r);
+      if (tid == 0 && n_exact) atomicAdd(p.stats + 5, (unsigned long long)n_exact);
+    }
     if (tid == 0) {
       atomicAdd(p.stats + 0, pairs_full);
       atomicAdd(p.stats + 1, t_full);
@@ -709,20 +752,20 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-// Per head_dim tile configuration (waves, 32-row blocks per wave, 32-key blocks per step).
+// Per head_dim tile configuration (waves, 32-row blocks per wave).
 template <int D>
 struct TileCfg {
-  static constexpr int NW = RA_FWD_NW, NB = RA_FWD_NB, MB = RA_FWD_MB;
+  static constexpr int NW = RA_FWD_NW, NB = 1;
 };
 template <>
 struct TileCfg<64> {  // the d = 64 tiles are too small to split over more than 4 waves
-  static constexpr int NW = 4, NB = 2, MB = 1;
+  static constexpr int NW = 4, NB = 2;
 };
 
 template <int D, typename OutT>
 hipError_t launch_one(FwdParams p, hipStream_t stream) {
   using T = TileCfg<D>;
-  using C = Cfg<D, T::NW, T::NB, T::MB>;
+  using C = Cfg<D, T::NW, T::NB>;
   p.n_qtiles = (int32_t)((p.n_loc + C::BQ - 1) / C::BQ);
   p.n_ktiles = (int32_t)((p.n_loc + C::BK - 1) / C::BK);
   p.n_pairs = (p.n_qtiles + 1) / 2;
@@ -730,8 +773,8 @@ hipError_t launch_one(FwdParams p, hipStream_t stream) {
   const int64_t grid = per_split * p.n_splits;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   p.grid_per_split = (int32_t)per_split;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, T::NW, T::NB, T::MB, OutT>), dim3((unsigned)grid),
-                     dim3(C::NT), 0, stream, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, T::NW, T::NB, OutT>), dim3((unsigned)grid), dim3(C::NT), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
@@ -740,11 +783,10 @@ hipError_t launch_one(FwdParams p, hipStream_t stream) {
 void tile_shape_bf16(int32_t head_dim, int32_t* tq, int32_t* tk) {
   if (head_dim == 64) {
     *tq = TileCfg<64>::NW * TileCfg<64>::NB * 32;
-    *tk = TileCfg<64>::MB * 32;
   } else {
     *tq = TileCfg<128>::NW * TileCfg<128>::NB * 32;
-    *tk = TileCfg<128>::MB * 32;
   }
+  *tk = 32;
 }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int32_t head_dim, int32_t out_dtype,

@@ -80,6 +80,7 @@ struct FwdParams {
   float scale_log2;    // scale * log2(e)
   int32_t sync_loads;  // wait for each batch of tile loads right after issuing it
   int32_t qo_natural;  // q / out / lse rows are global positions of [B, h_q, S, d] tensors
+  int32_t event_counts;  // stats has slots 4 and 5 (reference raises, exact recomputations)
   int64_t qo_rows;     // rows per (batch, head) of q / out / lse: S/c, or S when qo_natural
   // Split over the block list: n_splits groups of consecutive blocks, each
   // written as a partial to out / lse + split * part_stride (1: no split).

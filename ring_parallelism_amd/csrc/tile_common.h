@@ -13,6 +13,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) unsigned int lds_u32;
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format

@@ -90,7 +90,7 @@ def test_tile_shape():
     (dict(scale=0.0), ra.EINVAL, "scale"),
     (dict(scale=float("nan")), ra.EINVAL, "scale"),
     (dict(seq_len=1 << 31, n_shards=2), ra.EUNSUPPORTED, "2\\^31"),
-    (dict(flags=4), ra.EINVAL, "flags"),
+    (dict(flags=8), ra.EINVAL, "flags"),
     (dict(flags=ra.FLAG_SYNC_LOADS, in_dtype=ra.F32), ra.EUNSUPPORTED, "bf16 inputs only"),
 ])
 def test_descriptor_validation(kw, status, match):
