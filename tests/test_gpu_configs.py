@@ -99,6 +99,47 @@ def test_s128k_all_shards_sampled(problems):
         assert st.cpu().tolist() == expected_stats(p, r, tq, tk)
 
 
+def test_s128k_benched_launch_bf16_out_sampled(problems):
+    """The launch the benchmark times -- bf16 output -- against the oracle on
+    sampled rows of three shards (every query head of one KV group slot)."""
+    p = problems("s128k_c16_zigzag_16x1")
+    for r in (0, 7, 15):
+        say(f"s128k bf16-out rank {r}")
+        rows = workloads.sample_rows(p.n_loc, p.n_loc // 2, 248, 1000 + r)
+        heads = np.array([(3 * r) % p.Hq, (3 * r + 8) % p.Hq])
+        out, lse, _ = p.run(r, out_dtype=ra.BF16, with_stats=False)
+        ref_o, ref_l = p.reference(r, rows=rows, heads=heads)
+        compare(out, lse, ref_o, ref_l, rows=rows, heads=heads, tol=TOL["bf16"], bf16_out=True)
+        del out, lse
+
+
+def test_s128k_natural_order_q_out_sampled(problems):
+    """The fused gather/scatter at full size: Q read and bf16 out / lse written
+    at global positions of the natural-order 131 072-token tensors, compared
+    with the oracle at the sampled rows' positions for two ranks."""
+    import torch
+    from gpu_util import DEV, up
+    p = problems("s128k_c16_zigzag_16x1")
+    qn = up(p.q, p.dtype)
+    out_nat = torch.zeros((p.B, p.Hq, p.S, p.d), dtype=torch.bfloat16, device=DEV)
+    lse_nat = torch.zeros((p.B, p.Hq, p.S), dtype=torch.float32, device=DEV)
+    desc = p.desc(ra.BF16, True, flags=ra.FLAG_NATURAL_QO)
+    for r in (0, 11):
+        say(f"s128k natural q/out rank {r}")
+        owners = p.ring_owners(r)
+        ra.ring_attn_shard_fwd(desc, r, qn, [p.ks[j] for j in owners], [p.vs[j] for j in owners], out_nat, lse_nat,
+                               block_owner=owners)
+        torch.cuda.synchronize()
+        rows = workloads.sample_rows(p.n_loc, p.n_loc // 2, 248, 2000 + r)
+        pos = p.perm[r * p.n_loc + rows]
+        heads = np.array([r % p.Hq])
+        ref_o, ref_l = p.reference(r, rows=rows, heads=heads)
+        pos_t = torch.from_numpy(pos).to(DEV)
+        compare(out_nat[:, :, pos_t], lse_nat[:, :, pos_t], ref_o, ref_l, heads=heads, tol=TOL["bf16"],
+                bf16_out=True)
+    del qn, out_nat, lse_nat
+
+
 def test_s256k_one_shard_fused_partial_and_bidirectional(problems):
     p = problems("s256k_c32_zigzag_64x8")
     r = 0
@@ -124,3 +165,8 @@ def test_s256k_one_shard_fused_partial_and_bidirectional(problems):
     del fused, acc_o, acc_l
     say("s256k bidirectional")
     _sampled(p, r, heads, causal=False)
+    say("s256k fused causal, bf16 output (the timed launch)")
+    rows = workloads.sample_rows(p.n_loc, p.n_loc // 2, 248, 1000 + r)
+    out, lse, _ = p.run(r, out_dtype=ra.BF16, with_stats=False)
+    ref_o, ref_l = p.reference(r, rows=rows, heads=heads)
+    compare(out, lse, ref_o, ref_l, rows=rows, heads=heads, tol=TOL["bf16"], bf16_out=True)

@@ -145,6 +145,9 @@ def test_random_natural_order_q_out(case):
     rows = torch.from_numpy(p.perm[r * p.n_loc:(r + 1) * p.n_loc]).to(DEV)
     torch.cuda.synchronize()
     assert torch.equal(out_nat[:, :, rows], o) and torch.equal(lse_nat[:, :, rows], l)
+    # ... and both equal the oracle at the rank's global positions.
+    ref_o, ref_l = p.reference(r, causal=k["causal"])
+    compare(out_nat[:, :, rows], lse_nat[:, :, rows], ref_o, ref_l, tol=TOL[k["dtype"]])
     others = torch.ones(p.S, dtype=torch.bool, device=DEV)
     others[rows] = False
     assert torch.isnan(out_nat[:, :, others]).all() and torch.isnan(lse_nat[:, :, others]).all()

@@ -107,6 +107,32 @@ def test_natural_qo_matches_shard_layout(case):
     assert not torch.isnan(out_nat).any() and not torch.isnan(lse_nat).any()
 
 
+@pytest.mark.parametrize("case", [SMALL_CASES[i] for i in (0, 1, 3, 4, 5, 7, 9, 10, 11)],
+                         ids=lambda c: f"S{c[0]}_c{c[1]}_sp{c[2]}_d{c[6]}_{c[7]}_{'causal' if c[8] else 'full'}")
+def test_natural_qo_matches_oracle(case):
+    """Q read and out / lse written at global positions of natural-order
+    tensors ("Splitting the Sequence", intro: device k holds chunks k and
+    2c-1-k): after every rank has run, the natural-order tensors are compared
+    element by element with the oracle's full attention at every position, in
+    both output dtypes."""
+    S, c, split, B, Hq, Hkv, d, dtype, causal = case
+    p = Problem(S, c, split, B, Hq, Hkv, d, dtype, seed=S + c + 2)
+    qn = up(p.q, dtype)
+    ref_o, ref_l = oracle.attention(p.q, p.k, p.v, p.scale, causal)
+    for out_dtype in ([ra.F32] if dtype == "f32" else [ra.F32, ra.BF16]):
+        odt = torch.float32 if out_dtype == ra.F32 else torch.bfloat16
+        out_nat = torch.full((B, Hq, S, d), float("nan"), dtype=odt, device=DEV)
+        lse_nat = torch.full((B, Hq, S), float("nan"), dtype=torch.float32, device=DEV)
+        desc = p.desc(out_dtype, causal, flags=ra.FLAG_NATURAL_QO)
+        for r in range(c):
+            say(f"natural q/out vs oracle {case} out={out_dtype} rank {r}")
+            owners = p.ring_owners(r)
+            ra.ring_attn_shard_fwd(desc, r, qn, [p.ks[j] for j in owners], [p.vs[j] for j in owners], out_nat,
+                                   lse_nat, block_owner=owners)
+        torch.cuda.synchronize()
+        compare(out_nat, lse_nat, ref_o, ref_l, tol=TOL[dtype], bf16_out=out_dtype == ra.BF16)
+
+
 @pytest.mark.parametrize("S,c,split,B,Hq,Hkv,d,n_splits,out_dtype", [
     (4096, 4, ra.SPLIT_ZIGZAG, 1, 4, 1, 128, 2, ra.F32),
     (4096, 8, ra.SPLIT_CONTIGUOUS, 1, 4, 2, 128, 8, ra.F32),   # one block per group
