@@ -101,16 +101,47 @@ def measured_traffic():
     return float(fields["traffic_bytes_per_launch"])
 
 
+def measured_clock():
+    """Shader clock (GHz) the chip held during the attention kernel, from the
+    committed counter summary (GRBM_GUI_ACTIVE per XCD / kernel duration), or
+    None when the kernel source has changed since the counters were taken."""
+    import hashlib
+    prof = os.path.join(ROOT, "profiles", "fwd_bf16_s128k_c16_zigzag_mfma_counters.md")
+    src = os.path.join(ROOT, "ring_parallelism_amd", "csrc", "fwd_bf16.hip")
+    try:
+        fields = dict(line.split(": ", 1) for line in open(prof).read().splitlines() if ": " in line)
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if fields.get("source_sha256", "").strip() != sha or "held_clock_ghz" not in fields:
+        return None
+    return float(fields["held_clock_ghz"])
+
+
+def host_info():
+    """The host the run is on: CPU model and the core count the oracle uses."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cpu_count": os.cpu_count()}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="s128k_c16_zigzag_16x1", choices=sorted(workloads.WORKLOAD_BY_NAME))
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle CPU-baseline budget (0: skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle CPU-baseline budget (0: skip)")
     ap.add_argument("--suite", action="store_true",
                     help="instead of the headline line, print one JSON line per secondary measurement: "
-                         "MFMA probe, per-shard balance (32k tokens), warm/cold and overlap on/off "
+                         "per-shard balance (32k tokens), all shards in one launch (8k, 32k, 131k tokens), "
+                         "warm/cold and overlap on/off "
                          "(131k tokens), partial+merge and bidirectional passes (262k tokens), split-KV "
                          "decode, and every workload's GPU time beside the fp64 oracle's")
     ap.add_argument("--reps", type=int, default=10, help="timed repetitions per launch in --suite (after 3 warm-ups)")
@@ -127,6 +158,10 @@ def main():
         suite(args)
         return
     w = workloads.WORKLOAD_BY_NAME[args.workload]
+    # The CPU baseline runs first, bounded, so that the GPU leg that follows is
+    # one uninterrupted stretch of device work.
+    host = host_info()
+    cpu = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
     dev = torch.device("cuda:0")
     in_dt = ra.BF16 if w.dtype == "bf16" else ra.F32
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -185,15 +220,6 @@ def main():
         torch.cuda.synchronize()
         kernel_ms.extend(ev[r][0].elapsed_time(ev[r][1]) for r in range(c))
 
-    # The box's sustained bf16 MFMA rate (same instruction mix, no memory
-    # traffic): context for the fraction of the published peak.
-    nwg, pflop = ra.ring_attn_mfma_probe(2000)
-    sink = torch.empty(nwg * 512, dtype=torch.float32, device=dev)
-    probe_ms = timed(torch, lambda: ra.ring_attn_mfma_probe(2000, sink), 3)
-    probe_tf = pflop / (float(np.median(probe_ms)) / 1e3) / 1e12
-    probe_rnd_ms = timed(torch, lambda: ra.ring_attn_mfma_probe(2000, sink, random_operands=True), 3)
-    probe_rnd_tf = pflop / (float(np.median(probe_rnd_ms)) / 1e3) / 1e12
-
     pairs = [shard_pairs(w, r) for r in range(c)]               # per query head
     flop_step = sum(useful_flop(w, pr) for pr in pairs)
     pairs_counted = st[0] / args.steps
@@ -223,15 +249,13 @@ def main():
                      "median_launch_ms": round(float(np.median(kernel_ms)), 4),
                      "min_launch_ms": round(float(np.min(kernel_ms)), 4),
                      "launches_timed": len(kernel_ms),
-                     "probe_sustained_tflops": round(probe_tf, 1),
-                     "frac_of_probe": round(achieved / probe_tf, 4),
-                     "probe_random_operands_tflops": round(probe_rnd_tf, 1),
-                     "frac_of_probe_random": round(achieved / probe_rnd_tf, 4)},
+                     "held_shader_clock_ghz": measured_clock() if w.name == "s128k_c16_zigzag_16x1" else None},
         "stats_per_step": {"pairs": int(pairs_counted), "tiles_full": st[1] // args.steps,
                            "tiles_partial": st[2] // args.steps, "tiles_skipped": st[3] // args.steps},
     }
-    if args.cpu_seconds > 0:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
+    res["host"] = host
     print(json.dumps(res), flush=True)
 
 
@@ -284,17 +308,6 @@ def suite(args):
     dev = torch.device("cuda:0")
     reps = max(1, args.reps)
 
-    # Sustained bf16 MFMA rate of this device with the attention step's matrix mix.
-    nwg, flop = ra.ring_attn_mfma_probe(2000)
-    sink = torch.empty(nwg * 512, dtype=torch.float32, device=dev)
-    for rnd in (False, True):
-        ms = timed(torch, lambda: ra.ring_attn_mfma_probe(2000, sink, random_operands=rnd), reps)
-        tf = flop / (np.median(ms) / 1e3) / 1e12
-        emit({"measurement": "mfma_probe", "operands": "random N(0,1) bf16" if rnd else "fixed low-entropy",
-              "workgroups": nwg, "flop": flop, **stat(ms),
-              "tflops": round(tf, 1), "pct_of_nominal": round(100 * tf / PEAK_BF16_TFLOPS, 2),
-              "implied_clock_ghz_at_4096_flop_per_clk_per_cu": round(tf * 1e12 / (nwg * 4096) / 1e9, 3)})
-
     def fwd(w, desc, r, q, ks, vs, out, lse, owners=None):
         c = w.n_shards
         own = [(r - t) % c for t in range(c)] if owners is None else owners
@@ -341,19 +354,9 @@ def suite(args):
         st = stat(timed(torch, fwd(w, desc, 0, qs[0], ks, vs, out, lse), reps, sc))
         emit({"measurement": "shard_pass", "workload": w.name, "mode": mode, **st,
               "tflops": round(f0 / (st["median_ms"] / 1e3) / 1e12, 1)})
-    # Same launch on lower-entropy operands (a diagnostic of the power-limited
-    # clock, not a result): N(0, 0.1^2) and all-zero Q, K, V.
-    desc = ra.make_desc(w.seq_len, w.n_shards, w.split, w.batch, w.h_q, w.h_kv, w.head_dim, ra.BF16, ra.BF16,
-                        True, w.scale)
-    for label, f in (("operands N(0,0.1^2)", 0.1), ("operands all zero", 0.0)):
-        q2, k2, v2 = ((x.float() * f).to(torch.bfloat16) for x in (qs[0], ks, vs))
-        st = stat(timed(torch, fwd(w, desc, 0, q2, k2, v2, out, lse), reps))
-        tf = f0 / (st["median_ms"] / 1e3) / 1e12
-        emit({"measurement": "shard_pass", "workload": w.name, "mode": label, **st, "tflops": round(tf, 1),
-              "pct_of_nominal": round(100 * tf / PEAK_BF16_TFLOPS, 2)})
-        del q2, k2, v2
     del qs, ks, vs, scrub
 
+    all_shards_suite(torch, ra, dev, reps)
     split_suite(torch, ra, dev, reps)
     natural_step_suite(torch, ra, dev, reps)
     decode_suite(torch, ra, dev, reps)
@@ -407,6 +410,39 @@ def suite(args):
           "merge_roofline": {"bound": "hbm", "achieved": round(merge_bytes / (np.median(mm) / 1e3) / 1e9, 1),
                              "peak": 8000.0, "unit": "GB/s",
                              "frac": round(merge_bytes / (np.median(mm) / 1e3) / 1e9 / 8000.0, 4)}})
+
+
+def all_shards_suite(torch, ra, dev, reps):
+    """Every shard's ring pass in one launch (ring_attn_all_shards_fwd): the
+    8 192-token workload (all 8 shards), the 32 768-token one under each
+    placement (all 16 shards) and the 131 072-token one.  A shard of the small
+    workloads alone has too few query tiles to fill the device; together they
+    do.  Per-shard figures are the launch time divided by c (zig-zag shards
+    carry equal work)."""
+    names = ["s8k_c8_zigzag_gqa32x8", "s32k_c16_contig_16x1", "s32k_c16_zigzag_16x1", None, "s128k_c16_zigzag_16x1"]
+    for name in names:
+        if name is None:
+            w = workloads.WORKLOAD_BY_NAME["s32k_c16_zigzag_16x1"]
+            w = workloads.Workload(**{**w.__dict__, "name": "s32k_c16_striped_16x1", "split": workloads.SPLIT_STRIPED})
+        else:
+            w = workloads.WORKLOAD_BY_NAME[name]
+        c, n = w.n_shards, w.n_loc
+        g = torch.Generator(device=dev).manual_seed(w.seed)
+        rnd = lambda *shape: (torch.randn(shape, generator=g, device=dev) * w.sigma).to(torch.bfloat16)  # noqa: E731
+        qs = rnd(c, w.batch, w.h_q, n, w.head_dim)
+        ks, vs = rnd(c, w.batch, w.h_kv, n, w.head_dim), rnd(c, w.batch, w.h_kv, n, w.head_dim)
+        out = torch.empty_like(qs)
+        lse = torch.empty((c, w.batch, w.h_q, n), dtype=torch.float32, device=dev)
+        desc = ra.make_desc(w.seq_len, c, w.split, w.batch, w.h_q, w.h_kv, w.head_dim, ra.BF16, ra.BF16, w.causal,
+                            w.scale)
+        st = stat(timed(torch, lambda: ra.ring_attn_all_shards_fwd(desc, qs, list(ks), list(vs), out, lse), reps))
+        flop = sum(useful_flop(w, shard_pairs(w, r)) for r in range(c))
+        tf = flop / (st["median_ms"] / 1e3) / 1e12
+        emit({"measurement": "all_shards_one_launch", "workload": w.name,
+              "split": {0: "contiguous", 1: "zigzag", 2: "striped"}[w.split], "shards": c, **st,
+              "per_shard_ms": round(st["median_ms"] / c, 4), "useful_flop": flop, "tflops": round(tf, 1),
+              "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)})
+        del qs, ks, vs, out, lse
 
 
 def split_suite(torch, ra, dev, reps):

@@ -55,7 +55,7 @@ enum { RA_F32 = 0, RA_BF16 = 1 };
 
 #define RA_MAX_BLOCKS 128  /* ring blocks per ring_attn_shard_fwd call */
 #define RA_MAX_PARTS 64    /* partial results per ring_attn_merge call */
-#define RA_ABI_VERSION 2
+#define RA_ABI_VERSION 3
 
 typedef struct {
   int64_t seq_len;   /* S, global tokens; S % c == 0 (S % 2c == 0 for ZIGZAG) */
@@ -165,6 +165,29 @@ ra_status ring_attn_shard_fwd(const ra_attn_desc* desc, int32_t rank, const void
                               const void* const* k_blocks, const void* const* v_blocks,
                               void* out, float* lse, int64_t* stats, void* stream);
 
+/* Every shard's ring pass at once: on one GPU, the work all c devices of the
+ * ring do in one layer ("Splitting the Sequence", "One sequence, sixteen
+ * devices": each device's queries against every block; the notes, section
+ * 4).  Equivalent to ring_attn_shard_fwd for every rank r in [0, c) with the
+ * ring order, bitwise; with bf16 inputs it is a single launch, so shards too
+ * small to fill the device on their own (few query tiles per rank) still do.
+ *
+ * q_shards     : device [c, B, h_q, S/c, d] in_dtype, shard r at index r (the
+ *                layout zigzag_partition's gather writes); with
+ *                RA_FLAG_NATURAL_QO the natural-order [B, h_q, S, d].
+ * k_blocks,
+ * v_blocks     : host arrays of c device pointers; entry j is shard j's keys /
+ *                values [B, h_kv, S/c, d] (indexed by owner, not by step).
+ * out_shards   : device [c, B, h_q, S/c, d] out_dtype (natural order with the
+ *                flag: every row is written once).
+ * lse_shards   : device fp32 [c, B, h_q, S/c] (or [B, h_q, S]).
+ * stats        : as ring_attn_shard_fwd, summed over the ranks.
+ * Errors: as ring_attn_shard_fwd; RA_EUNSUPPORTED for c > RA_MAX_BLOCKS.
+ * fp32 inputs run one launch per rank. */
+ra_status ring_attn_all_shards_fwd(const ra_attn_desc* desc, const void* q_shards,
+                                   const void* const* k_blocks, const void* const* v_blocks,
+                                   void* out_shards, float* lse_shards, int64_t* stats, void* stream);
+
 /* Tile shape (query rows, keys) that ring_attn_shard_fwd uses for `desc`,
  * i.e. the unit its stats count.  Errors as for the descriptor checks. */
 ra_status ring_attn_tile_shape(const ra_attn_desc* desc, int32_t* tile_q, int32_t* tile_k);
@@ -250,24 +273,6 @@ const char* ring_attn_last_error(void);
 
 /* RA_ABI_VERSION of the loaded library. */
 int32_t ring_attn_abi_version(void);
-
-/* Calibration probe for the roofline: the matrix-core instruction mix of one
- * attention step (a dependent chain of eight v_mfma_f32_32x32x16_bf16 and
- * four chains of two, no memory traffic) run `iters` times by eight waves on
- * every compute unit, so that the sustained bf16 MFMA rate (and hence the
- * shader clock under matrix load) can be timed next to the attention kernel.
- * The rate depends on the operand values through the chip's power limit:
- * operands = 0 uses fixed low-entropy fragments, operands = 1 pseudo-random
- * N(0,1)-like bf16 values (the attention workloads' distribution).
- * Not part of the attention path.
- *
- * iters >= 1; sink (device float[*n_workgroups * 512], caller-owned) receives
- * the accumulators so that the work is not optimised away.  On success
- * *n_workgroups is the number of workgroups launched (the device's compute
- * unit count) and *flop the dense FLOP the launch performs.  Passing sink =
- * NULL only fills *n_workgroups and *flop (nothing is launched). */
-ra_status ring_attn_mfma_probe(int64_t iters, int32_t operands, float* sink, int32_t* n_workgroups,
-                               double* flop, void* stream);
 
 #ifdef __cplusplus
 }

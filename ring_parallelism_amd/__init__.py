@@ -30,7 +30,7 @@ LIB_PATH = os.environ.get("RING_ATTN_LIB") or os.path.join(os.path.dirname(os.pa
                                                            "libring_attn.so")
 
 EXPORTS = ("zigzag_partition", "zigzag_unpartition", "ring_attn_shard_fwd", "ring_attn_tile_shape",
-           "ring_attn_merge", "ring_attn_last_error", "ring_attn_abi_version", "ring_attn_mfma_probe",
+           "ring_attn_merge", "ring_attn_last_error", "ring_attn_abi_version", "ring_attn_all_shards_fwd",
            "ring_attn_merge_strided", "ring_attn_decode", "ring_attn_shard_fwd_split")
 
 
@@ -75,13 +75,13 @@ def lib():
     L.ring_attn_shard_fwd.argtypes = [ctypes.POINTER(AttnDesc), i32, vp, i32, vp, vp, vp, vp, vp, vp, vp]
     L.ring_attn_tile_shape.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.ring_attn_merge.argtypes = [i32, i32, i64, i32, i32, vp, i32, vp, vp, i32, vp, vp]
-    L.ring_attn_mfma_probe.argtypes = [i64, i32, vp, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double), vp]
+    L.ring_attn_all_shards_fwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp]
     L.ring_attn_merge_strided.argtypes = [i32, i32, i64, i32, i32, vp, i64, i32, vp, i64, vp, i32, vp, vp]
     L.ring_attn_decode.argtypes = [ctypes.POINTER(AttnDesc), vp, i32, vp, vp, i32, vp, vp, vp]
     L.ring_attn_shard_fwd_split.argtypes = [ctypes.POINTER(AttnDesc), i32, vp, i32, vp, vp, vp, i32, vp, vp, vp,
                                             vp, vp, vp]
     for name in ("zigzag_partition", "zigzag_unpartition", "ring_attn_shard_fwd",
-                 "ring_attn_tile_shape", "ring_attn_merge", "ring_attn_mfma_probe",
+                 "ring_attn_tile_shape", "ring_attn_merge", "ring_attn_all_shards_fwd",
                  "ring_attn_merge_strided", "ring_attn_decode", "ring_attn_shard_fwd_split"):
         getattr(L, name).restype = i32
     L.ring_attn_last_error.restype = ctypes.c_char_p
@@ -164,6 +164,20 @@ def ring_attn_shard_fwd(desc: AttnDesc, rank, q, k_blocks, v_blocks, out, lse, b
                                      _ptr(out), _ptr(lse), _ptr(stats), _stream(stream, q, out)))
 
 
+def ring_attn_all_shards_fwd(desc: AttnDesc, q_shards, k_blocks, v_blocks, out_shards, lse_shards, stats=None,
+                             stream=None):
+    """Every shard's ring pass at once: ``q_shards`` [c, B, h_q, S/c, d], block
+    ``j`` of ``k_blocks`` / ``v_blocks`` = shard j's keys / values, results in
+    ``out_shards`` [c, B, h_q, S/c, d] and ``lse_shards`` [c, B, h_q, S/c]."""
+    n = len(k_blocks)
+    if len(v_blocks) != n or n != desc.n_shards:
+        raise ValueError("k_blocks and v_blocks must hold one block per shard")
+    kp = (ctypes.c_void_p * n)(*[_ptr(t) for t in k_blocks])
+    vp = (ctypes.c_void_p * n)(*[_ptr(t) for t in v_blocks])
+    _check(lib().ring_attn_all_shards_fwd(ctypes.byref(desc), _ptr(q_shards), kp, vp, _ptr(out_shards),
+                                          _ptr(lse_shards), _ptr(stats), _stream(stream, q_shards, out_shards)))
+
+
 def ring_attn_shard_fwd_split(desc, rank, q, k_blocks, v_blocks, n_splits, work_out, work_lse, out, lse,
                               block_owner=None, stats=None, stream=None):
     """ring_attn_shard_fwd with the block list cut into ``n_splits`` concurrent
@@ -218,16 +232,6 @@ def ring_attn_decode(desc, q, k_blocks, v_blocks, n_splits, out_parts, lse_parts
     vp = (ctypes.c_void_p * max(n, 1))(*[_ptr(t) for t in v_blocks])
     _check(lib().ring_attn_decode(ctypes.byref(desc), _ptr(q), n, kp, vp, int(n_splits), _ptr(out_parts),
                                   _ptr(lse_parts), _stream(stream, q, out_parts)))
-
-
-def ring_attn_mfma_probe(iters, sink=None, random_operands=False, stream=None):
-    """Launch the matrix-core calibration probe (``sink``: device float32 tensor
-    of at least n_workgroups * 512 elements; None only queries).  Returns
-    ``(n_workgroups, flop)`` of the launch."""
-    nwg, flop = ctypes.c_int32(0), ctypes.c_double(0.0)
-    _check(lib().ring_attn_mfma_probe(int(iters), int(bool(random_operands)), _ptr(sink), ctypes.byref(nwg),
-                                      ctypes.byref(flop), _stream(stream, sink)))
-    return int(nwg.value), float(flop.value)
 
 
 def shard_tensor(x, n_shards, split, stream=None):

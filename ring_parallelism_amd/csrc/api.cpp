@@ -204,6 +204,54 @@ ra_status ring_attn_shard_fwd(const ra_attn_desc* desc, int32_t rank, const void
   return ok();
 }
 
+ra_status ring_attn_all_shards_fwd(const ra_attn_desc* desc, const void* q_shards, const void* const* k_blocks,
+                                   const void* const* v_blocks, void* out_shards, float* lse_shards,
+                                   int64_t* stats, void* stream) {
+  ra_status st = check_desc(desc);
+  if (st != RA_OK) return st;
+  const int32_t c = desc->n_shards;
+  if (c > RA_MAX_BLOCKS) return fail(RA_EUNSUPPORTED, "n_shards %d exceeds RA_MAX_BLOCKS (%d)", c, RA_MAX_BLOCKS);
+  const bool natural = (desc->flags & RA_FLAG_NATURAL_QO) != 0;
+  const int64_t n_loc = desc->seq_len / c;
+  const int64_t rows = (int64_t)desc->batch * desc->h_q * n_loc;  // per rank
+  const int64_t q_stride = natural ? 0 : rows * desc->head_dim;
+  const int64_t lse_stride = natural ? 0 : rows;
+  const size_t in_sz = desc->in_dtype == RA_F32 ? 4 : 2, out_sz = desc->out_dtype == RA_F32 ? 4 : 2;
+  if (!k_blocks || !v_blocks) return fail(RA_EINVAL, "k_blocks and v_blocks must be set");
+  int32_t ident[RA_MAX_BLOCKS];
+  for (int32_t j = 0; j < c; ++j) ident[j] = j;
+  if (desc->in_dtype == RA_F32) {
+    // fp32 inputs: one launch per rank (the parity path).
+    const void* kb[RA_MAX_BLOCKS];
+    const void* vb[RA_MAX_BLOCKS];
+    for (int32_t r = 0; r < c; ++r) {
+      for (int32_t t = 0; t < c; ++t) {
+        const int32_t j = (r - t + c) % c;
+        kb[t] = k_blocks[j];
+        vb[t] = v_blocks[j];
+      }
+      ra::FwdParams p;
+      st = shard_params(desc, r, q_shards ? (const char*)q_shards + r * q_stride * in_sz : nullptr, c, nullptr,
+                        kb, vb, out_shards ? (char*)out_shards + r * q_stride * out_sz : nullptr,
+                        lse_shards ? lse_shards + r * lse_stride : nullptr, stats, p);
+      if (st != RA_OK) return st;
+      hipError_t e = ra::launch_fwd_f32(p, desc->head_dim, (hipStream_t)stream);
+      if (e != hipSuccess) return fail(RA_EHIP, "shard_fwd launch failed: %s", hipGetErrorString(e));
+    }
+    return ok();
+  }
+  ra::FwdParams p;
+  st = shard_params(desc, 0, q_shards, c, ident, k_blocks, v_blocks, out_shards, lse_shards, stats, p);
+  if (st != RA_OK) return st;
+  p.all_ranks = 1;
+  p.rank_stride_q = q_stride;
+  p.rank_stride_out = q_stride;
+  p.rank_stride_lse = lse_stride;
+  hipError_t e = ra::launch_fwd_bf16(p, desc->head_dim, desc->out_dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RA_EHIP, "all-shards launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 ra_status ring_attn_shard_fwd_split(const ra_attn_desc* desc, int32_t rank, const void* q, int32_t n_blocks,
                                     const int32_t* block_owner, const void* const* k_blocks,
                                     const void* const* v_blocks, int32_t n_splits, float* work_out,
@@ -297,24 +345,6 @@ ra_status ring_attn_merge(int32_t batch, int32_t heads, int64_t rows, int32_t he
 }
 
 
-ra_status ring_attn_mfma_probe(int64_t iters, int32_t operands, float* sink, int32_t* n_workgroups,
-                               double* flop, void* stream) {
-  if (iters < 1) return fail(RA_EINVAL, "iters must be >= 1");
-  if (operands != 0 && operands != 1) return fail(RA_EINVAL, "operands must be 0 (fixed) or 1 (random)");
-  if (!n_workgroups || !flop) return fail(RA_EINVAL, "n_workgroups and flop must be set");
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return fail(RA_EHIP, "device query failed: %s", hipGetErrorString(e));
-  if (cus < 1) return fail(RA_EHIP, "device reports %d compute units", cus);
-  *n_workgroups = cus;
-  *flop = ra::mfma_probe_flop(iters, cus);
-  if (!sink) return ok();
-  if (!aligned(sink, 4)) return fail(RA_EINVAL, "sink must be 4-byte aligned");
-  e = ra::launch_mfma_probe(iters, operands, sink, cus, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(RA_EHIP, "probe launch failed: %s", hipGetErrorString(e));
-  return ok();
-}
 
 ra_status ring_attn_merge_strided(int32_t batch, int32_t heads, int64_t rows, int32_t head_dim,
                                   int32_t n_parts, const void* outs, int64_t out_stride, int32_t parts_dtype,

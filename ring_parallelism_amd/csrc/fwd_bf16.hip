@@ -149,14 +149,23 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
   // items on one XCD.
   const int n_wg = gridDim.x;
   const int bid = blockIdx.x;
-  const int wl_all = (n_wg % 8 == 0) ? (bid % 8) * (n_wg / 8) + bid / 8 : bid;
+  const int wl_grid = (n_wg % 8 == 0) ? (bid % 8) * (n_wg / 8) + bid / 8 : bid;
+  // Every rank's ring pass in one launch: the rank is the leading part of the
+  // work index, its q / out / lse sit at rank strides, and its block order is
+  // the ring order (owner (rank - t) mod c, block table indexed by owner).
+  const int rank = p.all_ranks ? wl_grid / p.grid_per_rank : p.rank;
+  const int wl_all = p.all_ranks ? wl_grid % p.grid_per_rank : wl_grid;
+  auto owner_of = [&](int t) { return p.all_ranks ? (rank + p.c - t) % p.c : p.owner[t]; };
+  auto block_k = [&](int t) { return p.k[p.all_ranks ? (rank + p.c - t) % p.c : t]; };
+  auto block_v = [&](int t) { return p.v[p.all_ranks ? (rank + p.c - t) % p.c : t]; };
   // Split of the block list (one group when n_splits = 1): this workgroup
   // folds blocks [t0, t1) and writes its own partial result.
   const int split = wl_all / p.grid_per_split;
   const int wl = wl_all % p.grid_per_split;
   const int t0 = split * p.n_blocks / p.n_splits, t1 = (split + 1) * p.n_blocks / p.n_splits;
-  OutT* const out_base = (OutT*)p.out + split * p.part_stride_out;
-  float* const lse_base = p.lse + split * p.part_stride_lse;
+  OutT* const out_base = (OutT*)p.out + split * p.part_stride_out + rank * p.rank_stride_out;
+  float* const lse_base = p.lse + split * p.part_stride_lse + rank * p.rank_stride_lse;
+  const __bf16* const q_base = (const __bf16*)p.q + rank * p.rank_stride_q;
   const int h = wl % p.h_q;
   const int pair = (wl / p.h_q) % p.n_pairs;
   const int b = wl / (p.h_q * p.n_pairs);
@@ -208,8 +217,8 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
     const int i0 = qt * C::BQ;
     const bool rows_full = i0 + C::BQ <= n_loc;
     const int last_row = (rows_full ? i0 + C::BQ : n_loc) - 1;
-    const int pos_first = token_pos32(p.rank, i0, n_loc, p.c, p.split);
-    const int pos_last = token_pos32(p.rank, last_row, n_loc, p.c, p.split);
+    const int pos_first = token_pos32(rank, i0, n_loc, p.c, p.split);
+    const int pos_last = token_pos32(rank, last_row, n_loc, p.c, p.split);
 
     // Query rows of this lane (one per 32-block) and their positions; Q^T
     // operand fragments stay in registers for the whole pass.
@@ -219,9 +228,9 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
     for (int nb = 0; nb < NB; ++nb) {
       const int row = i0 + (wave * NB + nb) * 32 + lc;
       const bool ok = row < n_loc;
-      posq[nb] = ok ? token_pos32(p.rank, row, n_loc, p.c, p.split) : -1;  // -1: past the shard end
+      posq[nb] = ok ? token_pos32(rank, row, n_loc, p.c, p.split) : -1;  // -1: past the shard end
       const int qrow = ok ? (p.qo_natural ? posq[nb] : row) : 0;
-      const __bf16* qp = (const __bf16*)p.q + (q_off + qrow) * D + g * 8;
+      const __bf16* qp = q_base + (q_off + qrow) * D + g * 8;
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) qreg[nb][s] = ok ? *(const bf16x8*)(qp + s * 16) : bf16x8{};
     }
@@ -253,9 +262,9 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
       const __bf16* vb;
     };
     auto block_counts = [&](Tile& x) {
-      const int j = p.owner[x.t];
-      x.kb = (const __bf16*)p.k[x.t] + kv_off;
-      x.vb = (const __bf16*)p.v[x.t] + kv_off;
+      const int j = owner_of(x.t);
+      x.kb = (const __bf16*)block_k(x.t) + kv_off;
+      x.vb = (const __bf16*)block_v(x.t) + kv_off;
       const int c_last = p.causal ? count_upto32(j, pos_last, n_loc, p.c, p.split) : n_loc;
       const int c_first = p.causal ? count_upto32(j, pos_first, n_loc, p.c, p.split) : n_loc;
       x.vis = (c_last + kBK - 1) / kBK;
@@ -322,7 +331,7 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
     // count_upto(j, pos_q) rows: one bound per row.  Accumulator element i is
     // key (i/4)*8 + g*4 + i%4 of the tile.
     auto mask = [&](f32x16 (&sacc)[NB], const Tile& x) {
-      const int j = p.owner[x.t];
+      const int j = owner_of(x.t);
       int lim[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -553,7 +562,7 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
     // first tile gives every row a finite reference) unless a causal mask
     // hides it from the tile's first row (positions ascend).
     const bool fast = n_tiles > 0 &&
-                      (!p.causal || count_upto32(p.owner[first.t], pos_first, n_loc, p.c, p.split) >= 1);
+                      (!p.causal || count_upto32(owner_of(first.t), pos_first, n_loc, p.c, p.split) >= 1);
     if (fast) {
       Tile ld = first;
       static_for<0, C::AHEAD>([&](auto I) {
@@ -625,7 +634,9 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
           // A bare s_barrier: a fenced one would wait for every load in
           // flight.  Every LDS read of a stage the next group refills was
           // awaited inside its step.
-          if constexpr (C::LATE > 0) {
+          // (vmcnt counts in issue order: the allowance holds only when this
+          // group issued all G tiles' loads; near the end it issued fewer.)
+          if (C::LATE > 0 && i + C::AHEAD < n_tiles) {
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::LATE * 2 * C::LOADS) : "memory");
           } else {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -718,10 +729,10 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
       const int i0 = qt * C::BQ;
       const bool rows_full = i0 + C::BQ <= n_loc;
       const int last_row = (rows_full ? i0 + C::BQ : n_loc) - 1;
-      const int pos_first = token_pos32(p.rank, i0, n_loc, p.c, p.split);
-      const int pos_last = token_pos32(p.rank, last_row, n_loc, p.c, p.split);
+      const int pos_first = token_pos32(rank, i0, n_loc, p.c, p.split);
+      const int pos_last = token_pos32(rank, last_row, n_loc, p.c, p.split);
       for (int t = t0; t < t1; ++t) {
-        const int j = p.owner[t];
+        const int j = owner_of(t);
         const int c_last = p.causal ? count_upto32(j, pos_last, n_loc, p.c, p.split) : n_loc;
         const int c_first = p.causal ? count_upto32(j, pos_first, n_loc, p.c, p.split) : n_loc;
         const int n_vis = (c_last + kBK - 1) / kBK;
@@ -773,7 +784,13 @@ hipError_t launch_one(FwdParams p, hipStream_t stream) {
   const int64_t grid = per_split * p.n_splits;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   p.grid_per_split = (int32_t)per_split;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, T::NW, T::NB, OutT>), dim3((unsigned)grid), dim3(C::NT), 0,
+  const int64_t per_rank = per_split * p.n_splits;
+  if (p.all_ranks) {
+    if (per_rank * p.c > 0x7fffffff) return hipErrorInvalidConfiguration;
+    p.grid_per_rank = (int32_t)per_rank;
+  }
+  const int64_t grid_all = p.all_ranks ? per_rank * p.c : grid;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, T::NW, T::NB, OutT>), dim3((unsigned)grid_all), dim3(C::NT), 0,
                      stream, p);
   return hipGetLastError();
 }

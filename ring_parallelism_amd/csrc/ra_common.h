@@ -86,6 +86,11 @@ struct FwdParams {
   // written as a partial to out / lse + split * part_stride (1: no split).
   int32_t n_splits, grid_per_split;
   int64_t part_stride_out, part_stride_lse;
+  // Every rank in one launch (all_ranks != 0): rank r's q / out / lse start
+  // r * rank_stride_* elements in, its blocks follow the ring order and
+  // k[] / v[] are indexed by owner.
+  int32_t all_ranks, grid_per_rank;
+  int64_t rank_stride_q, rank_stride_out, rank_stride_lse;
   int32_t owner[RA_MAX_BLOCKS];
   const void* k[RA_MAX_BLOCKS];
   const void* v[RA_MAX_BLOCKS];
@@ -133,8 +138,5 @@ hipError_t launch_merge(const MergeParams& p, int32_t parts_dtype, int32_t out_d
 void tile_shape_f32(int32_t head_dim, int32_t* tq, int32_t* tk);
 void tile_shape_bf16(int32_t head_dim, int32_t* tq, int32_t* tk);
 hipError_t launch_decode_bf16(const DecodeParams& p, int32_t head_dim, hipStream_t stream);
-hipError_t launch_mfma_probe(int64_t iters, int32_t mode, float* sink, int32_t n_workgroups, hipStream_t stream);
-constexpr int kProbeThreads = 512;  // eight waves per workgroup
-double mfma_probe_flop(int64_t iters, int32_t n_workgroups);
 
 }  // namespace ra

@@ -121,6 +121,25 @@ def test_shard_fwd_argument_validation():
         ra.ring_attn_shard_fwd(d, 0, FAKE, kb, kb[:3], FAKE, FAKE)
 
 
+def test_all_shards_validation():
+    d = good_desc()
+    kb = [FAKE] * 4
+    expect(ra.EINVAL, ra.ring_attn_all_shards_fwd, d, None, kb, kb, FAKE, FAKE, match="q, out")
+    expect(ra.EINVAL, ra.ring_attn_all_shards_fwd, d, FAKE, kb, kb, None, FAKE, match="q, out")
+    expect(ra.EINVAL, ra.ring_attn_all_shards_fwd, d, FAKE, kb, kb, FAKE, None, match="q, out")
+    expect(ra.EINVAL, ra.ring_attn_all_shards_fwd, d, FAKE + 8, kb, kb, FAKE, FAKE, match="aligned")
+    expect(ra.EINVAL, ra.ring_attn_all_shards_fwd, d, FAKE, [FAKE, None, FAKE, FAKE], kb, FAKE, FAKE, match="NULL")
+    expect(ra.EINVAL, ra.ring_attn_all_shards_fwd, d, FAKE, kb, kb, FAKE, FAKE, stats=FAKE + 4, match="stats")
+    expect(ra.EINVAL, ra.ring_attn_all_shards_fwd, good_desc(seq_len=0), FAKE, kb, kb, FAKE, FAKE, match="seq_len")
+    with pytest.raises(ValueError):
+        ra.ring_attn_all_shards_fwd(d, FAKE, kb[:3], kb[:3], FAKE, FAKE)
+    L = ra.lib()
+    assert L.ring_attn_all_shards_fwd(ctypes.byref(d), FAKE, None, None, FAKE, FAKE, None, None) == ra.EINVAL
+    big = good_desc(seq_len=256 * 200, n_shards=200, split=ra.SPLIT_CONTIGUOUS)
+    kb200 = [FAKE] * 200
+    expect(ra.EUNSUPPORTED, ra.ring_attn_all_shards_fwd, big, FAKE, kb200, kb200, FAKE, FAKE, match="RA_MAX_BLOCKS")
+
+
 def test_too_many_blocks():
     d = good_desc(seq_len=256 * 200, n_shards=200, split=ra.SPLIT_CONTIGUOUS)
     kb = [FAKE] * 129
@@ -182,13 +201,6 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(ra, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(ImportError):
         ra.lib()
-
-
-def test_mfma_probe_validation():
-    expect(ra.EINVAL, ra.ring_attn_mfma_probe, 0, match="iters")
-    L = ra.lib()
-    assert L.ring_attn_mfma_probe(1, 0, None, None, None, None) == ra.EINVAL
-    assert L.ring_attn_mfma_probe(1, 2, None, None, None, None) == ra.EINVAL
 
 
 def test_decode_validation():

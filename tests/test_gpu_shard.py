@@ -207,18 +207,6 @@ def test_sync_loads_flag_is_bitwise_neutral():
         assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(s1, s2)
 
 
-def test_mfma_probe_runs():
-    nwg, flop = ra.ring_attn_mfma_probe(4)
-    assert nwg >= 1 and flop == 2.0 * 32 * 32 * 16 * 16 * 4 * 8 * nwg
-    sink = torch.full((nwg * 512,), float("nan"), dtype=torch.float32, device=DEV)
-    say("mfma probe")
-    for rnd in (False, True):
-        sink.fill_(float("nan"))
-        assert ra.ring_attn_mfma_probe(4, sink, random_operands=rnd) == (nwg, flop)
-        torch.cuda.synchronize()
-        assert torch.isfinite(sink).all()
-
-
 # ---------------------------------------------------------------- partial results and merge
 
 @pytest.mark.parametrize("dtype,split", [("bf16", ra.SPLIT_ZIGZAG), ("f32", ra.SPLIT_CONTIGUOUS), ("bf16", ra.SPLIT_CONTIGUOUS)])
