@@ -155,9 +155,11 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
   // the ring order (owner (rank - t) mod c, block table indexed by owner).
   const int rank = p.all_ranks ? wl_grid / p.grid_per_rank : p.rank;
   const int wl_all = p.all_ranks ? wl_grid % p.grid_per_rank : wl_grid;
-  auto owner_of = [&](int t) { return p.all_ranks ? (rank + p.c - t) % p.c : p.owner[t]; };
-  auto block_k = [&](int t) { return p.k[p.all_ranks ? (rank + p.c - t) % p.c : t]; };
-  auto block_v = [&](int t) { return p.v[p.all_ranks ? (rank + p.c - t) % p.c : t]; };
+  // (0 <= rank, t < c, so (rank - t) mod c needs no division.)
+  auto ring_owner = [&](int t) { return rank >= t ? rank - t : rank - t + p.c; };
+  auto owner_of = [&](int t) { return p.all_ranks ? ring_owner(t) : p.owner[t]; };
+  auto block_k = [&](int t) { return p.k[p.all_ranks ? ring_owner(t) : t]; };
+  auto block_v = [&](int t) { return p.v[p.all_ranks ? ring_owner(t) : t]; };
   // Split of the block list (one group when n_splits = 1): this workgroup
   // folds blocks [t0, t1) and writes its own partial result.
   const int split = wl_all / p.grid_per_split;
