@@ -233,6 +233,27 @@ ra_status ring_attn_shard_fwd_split(const ra_attn_desc* desc, int32_t rank, cons
                                     const void* const* v_blocks, int32_t n_splits, float* work_out,
                                     float* work_lse, void* out, float* lse, int64_t* stats, void* stream);
 
+/* ring_attn_shard_fwd_split without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The partial results live in a static
+ * device array of the library -- RA_NOALLOC_MAX_PARTIAL_FLOATS floats for the
+ * partial outputs and RA_NOALLOC_MAX_LSE_FLOATS for their lse, 64.5 MiB that
+ * each GPU the library runs on holds until the process ends -- so the call
+ * allocates nothing.  n_splits * B * h_q * S/c * head_dim beyond the first
+ * limit (or n_splits * B * h_q * S/c beyond the second) is RA_EINVAL with a
+ * message; 4 splits of the 8 192-token (32 / 8 heads) and 32 768-token
+ * (16 / 1 heads) shards fit exactly.  All calls on one GPU share its array:
+ * calls that may overlap on one GPU (other streams, other host threads) race
+ * and must be serialised by the caller.  Other arguments, results and errors
+ * as ring_attn_shard_fwd_split. */
+#define RA_NOALLOC_MAX_PARTIAL_FLOATS (1 << 24)
+#define RA_NOALLOC_MAX_LSE_FLOATS (1 << 17)
+ra_status ring_attn_shard_fwd_split_noalloc(const ra_attn_desc* desc, int32_t rank, const void* q,
+                                            int32_t n_blocks, const int32_t* block_owner,
+                                            const void* const* k_blocks, const void* const* v_blocks,
+                                            int32_t n_splits, void* out, float* lse, int64_t* stats,
+                                            void* stream);
+
 /* ring_attn_merge with the parts in one buffer: part k's out starts
  * out_stride elements after part k-1's (parts_dtype elements, out_stride >=
  * batch*heads*rows*head_dim) and its lse lse_stride values after part k-1's

@@ -31,6 +31,7 @@ LIB_PATH = os.environ.get("RING_ATTN_LIB") or os.path.join(os.path.dirname(os.pa
 
 EXPORTS = ("zigzag_partition", "zigzag_unpartition", "ring_attn_shard_fwd", "ring_attn_tile_shape",
            "ring_attn_merge", "ring_attn_last_error", "ring_attn_abi_version", "ring_attn_all_shards_fwd",
+           "ring_attn_shard_fwd_split_noalloc",
            "ring_attn_merge_strided", "ring_attn_decode", "ring_attn_shard_fwd_split")
 
 
@@ -76,13 +77,16 @@ def lib():
     L.ring_attn_tile_shape.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.ring_attn_merge.argtypes = [i32, i32, i64, i32, i32, vp, i32, vp, vp, i32, vp, vp]
     L.ring_attn_all_shards_fwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp]
+    L.ring_attn_shard_fwd_split_noalloc.argtypes = [ctypes.POINTER(AttnDesc), i32, vp, i32, vp, vp, vp, i32, vp, vp,
+                                                    vp, vp]
     L.ring_attn_merge_strided.argtypes = [i32, i32, i64, i32, i32, vp, i64, i32, vp, i64, vp, i32, vp, vp]
     L.ring_attn_decode.argtypes = [ctypes.POINTER(AttnDesc), vp, i32, vp, vp, i32, vp, vp, vp]
     L.ring_attn_shard_fwd_split.argtypes = [ctypes.POINTER(AttnDesc), i32, vp, i32, vp, vp, vp, i32, vp, vp, vp,
                                             vp, vp, vp]
     for name in ("zigzag_partition", "zigzag_unpartition", "ring_attn_shard_fwd",
                  "ring_attn_tile_shape", "ring_attn_merge", "ring_attn_all_shards_fwd",
-                 "ring_attn_merge_strided", "ring_attn_decode", "ring_attn_shard_fwd_split"):
+                 "ring_attn_merge_strided", "ring_attn_decode", "ring_attn_shard_fwd_split",
+                 "ring_attn_shard_fwd_split_noalloc"):
         getattr(L, name).restype = i32
     L.ring_attn_last_error.restype = ctypes.c_char_p
     L.ring_attn_abi_version.restype = i32
@@ -196,6 +200,26 @@ def ring_attn_shard_fwd_split(desc, rank, q, k_blocks, v_blocks, n_splits, work_
     _check(lib().ring_attn_shard_fwd_split(ctypes.byref(desc), int(rank), _ptr(q), n, owners, kp, vp, int(n_splits),
                                            _ptr(work_out), _ptr(work_lse), _ptr(out), _ptr(lse), _ptr(stats),
                                            _stream(stream, q, out)))
+
+
+def ring_attn_shard_fwd_split_noalloc(desc, rank, q, k_blocks, v_blocks, n_splits, out, lse, block_owner=None,
+                                      stats=None, stream=None):
+    """ring_attn_shard_fwd_split with the partials in the library's static
+    device scratch (no workspace, no allocation; overlapping calls on one GPU
+    race)."""
+    n = len(k_blocks)
+    if len(v_blocks) != n:
+        raise ValueError("k_blocks and v_blocks differ in length")
+    kp = (ctypes.c_void_p * max(n, 1))(*[_ptr(t) for t in k_blocks])
+    vp = (ctypes.c_void_p * max(n, 1))(*[_ptr(t) for t in v_blocks])
+    owners = None
+    if block_owner is not None:
+        if len(block_owner) != n:
+            raise ValueError("block_owner and k_blocks differ in length")
+        owners = (ctypes.c_int32 * n)(*[int(x) for x in block_owner])
+    _check(lib().ring_attn_shard_fwd_split_noalloc(ctypes.byref(desc), int(rank), _ptr(q), n, owners, kp, vp,
+                                                   int(n_splits), _ptr(out), _ptr(lse), _ptr(stats),
+                                                   _stream(stream, q, out)))
 
 
 def ring_attn_merge(batch, heads, rows, head_dim, outs, parts_dtype, lses, out, out_dtype, lse,

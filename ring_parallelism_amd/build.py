@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libring_attn.so")
-SOURCES = ["api.cpp", "partition.hip", "fwd_f32.hip", "fwd_bf16.hip", "merge.hip", "decode.hip"]
+SOURCES = ["api.cpp", "partition.hip", "fwd_f32.hip", "fwd_bf16.hip", "merge.hip", "decode.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -25,6 +25,20 @@ ra_status ok() {
   return RA_OK;
 }
 
+}  // namespace
+
+namespace ra {
+ra_status set_error(ra_status code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+}  // namespace ra
+
+namespace {
+
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 ra_status check_split(int64_t S, int32_t c, int32_t split) {

@@ -126,6 +126,9 @@ struct DecodeParams {
   const void* v[RA_MAX_BLOCKS];
 };
 
+// Records the thread's last-error message; returns code.
+ra_status set_error(ra_status code, const char* fmt, ...);
+
 // Launchers (defined in the kernel translation units).
 hipError_t launch_partition(int64_t S, int32_t c, int32_t split, int64_t* perm, const void* src,
                             void* dst, int64_t outer, int64_t inner_bytes, bool inverse,
