@@ -150,11 +150,25 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
   const int n_wg = gridDim.x;
   const int bid = blockIdx.x;
   const int wl_grid = (n_wg % 8 == 0) ? (bid % 8) * (n_wg / 8) + bid / 8 : bid;
-  // Every rank's ring pass in one launch: the rank is the leading part of the
-  // work index, its q / out / lse sit at rank strides, and its block order is
-  // the ring order (owner (rank - t) mod c, block table indexed by owner).
-  const int rank = p.all_ranks ? wl_grid / p.grid_per_rank : p.rank;
-  const int wl_all = p.all_ranks ? wl_grid % p.grid_per_rank : wl_grid;
+  // Every rank's ring pass in one launch: q / out / lse of a rank sit at rank
+  // strides, and its block order is the ring order (owner (rank - t) mod c,
+  // block table indexed by owner).  Each XCD takes the same slice of every
+  // rank's work items -- so that the XCDs finish together even where the
+  // ranks' work differs (causal contiguous placement) and neighbouring heads,
+  // which share a key/value head, stay on one L2 -- in decreasing rank order,
+  // the heaviest first under causal contiguous placement.
+  int rank = p.rank, wl_all = wl_grid;
+  if (p.all_ranks) {
+    if (n_wg % 8 == 0 && p.grid_per_rank % 8 == 0) {
+      const int per_xcd = p.grid_per_rank / 8;  // items of one rank on one XCD
+      const int u = bid / 8;                    // dispatch order inside the XCD
+      rank = p.c - 1 - u / per_xcd;
+      wl_all = (bid % 8) * per_xcd + u % per_xcd;
+    } else {
+      rank = wl_grid / p.grid_per_rank;
+      wl_all = wl_grid % p.grid_per_rank;
+    }
+  }
   // (0 <= rank, t < c, so (rank - t) mod c needs no division.)
   auto ring_owner = [&](int t) { return rank >= t ? rank - t : rank - t + p.c; };
   auto owner_of = [&](int t) { return p.all_ranks ? ring_owner(t) : p.owner[t]; };

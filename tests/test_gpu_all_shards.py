@@ -24,6 +24,10 @@ CASES = [
     (512, 4, ra.SPLIT_ZIGZAG, 1, 6, 3, 64, "bf16", True),         # d = 64
     (8, 2, ra.SPLIT_ZIGZAG, 1, 2, 1, 128, "bf16", True),          # 2-token chunks
     (1024, 4, ra.SPLIT_CONTIGUOUS, 1, 4, 1, 64, "f32", True),     # fp32: per-rank launches
+    # 16 work items per rank: each XCD takes a slice of every rank (heaviest
+    # rank first) rather than whole ranks.
+    (4096, 4, ra.SPLIT_CONTIGUOUS, 1, 8, 2, 128, "bf16", True),
+    (4096, 4, ra.SPLIT_ZIGZAG, 2, 4, 4, 128, "bf16", True),
 ]
 
 
