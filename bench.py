@@ -145,7 +145,17 @@ def main():
                          "(131k tokens), partial+merge and bidirectional passes (262k tokens), split-KV "
                          "decode, and every workload's GPU time beside the fp64 oracle's")
     ap.add_argument("--reps", type=int, default=10, help="timed repetitions per launch in --suite (after 3 warm-ups)")
+    ap.add_argument("--traffic", action="store_true",
+                    help="run the kernels whose memory traffic is measured (under rocprofv3 --pmc): a plain "
+                         "conversion copy, the shard gather of Q, a two-part merge and the benchmarked shard pass, "
+                         f"{TRAFFIC_DISPATCHES} dispatches each")
+    ap.add_argument("--counters-report", nargs="+", metavar="DIR",
+                    help="summarise rocprofv3 counter CSVs under these directories for the --traffic kernels: "
+                         "bytes per dispatch from request counts by request size, beside the algorithmic bytes")
     args = ap.parse_args()
+    if args.counters_report:
+        counters_report(args.counters_report)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the ring: run with --gpus 1 (got {args.gpus}); "
               "the multi-GPU ring is not implemented here", file=sys.stderr)
@@ -156,6 +166,9 @@ def main():
 
     if args.suite:
         suite(args)
+        return
+    if args.traffic:
+        traffic_run()
         return
     w = workloads.WORKLOAD_BY_NAME[args.workload]
     # The CPU baseline runs first, bounded, so that the GPU leg that follows is
@@ -257,6 +270,105 @@ def main():
         res["cpu_baseline"] = cpu
     res["host"] = host
     print(json.dumps(res), flush=True)
+
+
+# Memory-traffic measurement.  The L2 (TCC) counts the requests it sends to
+# the memory side by size (32, 64 or 128 bytes for reads; 32 or 64 for
+# writes), so bytes = sum of count x size, with no calibration factor.  The
+# kernels of known byte counts run beside the attention launch to check that.
+TRAFFIC_WORKLOAD = "s128k_c16_zigzag_16x1"
+TRAFFIC_DISPATCHES = 3
+TRAFFIC_PASSES = {
+    "reads": ["TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum"],
+    "writes": ["TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "TCC_EA0_RDREQ_DRAM_sum", "TCC_EA0_WRREQ_DRAM_sum"],
+}
+
+
+def traffic_known(w):
+    """(label, kernel-name substring, algorithmic read bytes, write bytes) per
+    dispatch of the kernels traffic_run launches."""
+    esz = 2
+    q_all = w.batch * w.h_q * w.seq_len * w.head_dim * esz
+    kv_all = w.batch * w.h_kv * w.seq_len * w.head_dim * esz
+    rows = w.batch * w.h_q * w.n_loc
+    part = rows * w.head_dim * 4 + rows * 4          # one fp32 partial: out + lse
+    return [
+        ("conversion copy of Q, bf16 -> fp32 (torch)", "copy", q_all, 2 * q_all),
+        ("shard gather of Q (zigzag_partition)", "move_rows_kernel", q_all, q_all),
+        ("merge of two fp32 partials (ring_attn_merge_strided)", "merge_kernel", 2 * part, part),
+        ("shard pass, rank 0 (ring_attn_shard_fwd, bf16 out)", "fwd_bf16_kernel",
+         rows * w.head_dim * esz + 2 * kv_all, rows * w.head_dim * esz + rows * 4),
+    ]
+
+
+def traffic_run():
+    """The --traffic kernels, TRAFFIC_DISPATCHES launches each, on the
+    131 072-token workload's shapes (inputs drawn on the device)."""
+    import torch
+    import ring_parallelism_amd as ra
+    w = workloads.WORKLOAD_BY_NAME[TRAFFIC_WORKLOAD]
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(w.seed)
+    c, n = w.n_shards, w.n_loc
+    rnd = lambda *shape: (torch.randn(shape, generator=g, device=dev) * w.sigma).to(torch.bfloat16)  # noqa: E731
+    qn = rnd(w.batch, w.h_q, w.seq_len, w.head_dim)
+    q32 = torch.empty(qn.shape, dtype=torch.float32, device=dev)
+    qs = torch.empty((c, w.batch, w.h_q, n, w.head_dim), dtype=torch.bfloat16, device=dev)
+    parts = torch.randn((2, w.batch, w.h_q, n, w.head_dim), generator=g, device=dev)
+    part_lse = torch.randn((2, w.batch, w.h_q, n), generator=g, device=dev)
+    m_out = torch.empty(parts.shape[1:], dtype=torch.float32, device=dev)
+    m_lse = torch.empty(part_lse.shape[1:], dtype=torch.float32, device=dev)
+    ks = rnd(c, w.batch, w.h_kv, n, w.head_dim)
+    vs = rnd(c, w.batch, w.h_kv, n, w.head_dim)
+    out = torch.empty((w.batch, w.h_q, n, w.head_dim), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.batch, w.h_q, n), dtype=torch.float32, device=dev)
+    stats = torch.zeros(4, dtype=torch.int64, device=dev)
+    desc = ra.make_desc(w.seq_len, c, w.split, w.batch, w.h_q, w.h_kv, w.head_dim, ra.BF16, ra.BF16, w.causal, w.scale)
+    own = [(0 - t) % c for t in range(c)]
+    torch.cuda.synchronize()
+    for _ in range(TRAFFIC_DISPATCHES):
+        q32.copy_(qn)
+        ra.zigzag_partition(w.seq_len, c, w.split, None, qn, qs, w.batch * w.h_q, w.head_dim * 2)
+        ra.ring_attn_merge_strided(w.batch, w.h_q, n, w.head_dim, parts, ra.F32, part_lse, m_out, ra.F32, m_lse)
+        ra.ring_attn_shard_fwd(desc, 0, qs[0], [ks[j] for j in own], [vs[j] for j in own], out, lse, stats=stats)
+        torch.cuda.synchronize()
+    print(json.dumps({"traffic_run": w.name, "dispatches_each": TRAFFIC_DISPATCHES}), flush=True)
+
+
+def counters_report(dirs):
+    """Per-dispatch means of the TRAFFIC_PASSES counters for the --traffic
+    kernels, bytes from request counts x request sizes."""
+    import csv
+    import glob
+    vals = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                vals.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    w = workloads.WORKLOAD_BY_NAME[TRAFFIC_WORKLOAD]
+    rows = []
+    for label, sub, alg_r, alg_w in traffic_known(w):
+        m, n_disp = {}, 0
+        for (name, counter), v in vals.items():
+            if sub in name and "distribution" not in name:
+                m[counter] = float(np.mean(v))
+                n_disp = max(n_disp, len(v))
+        if not m:
+            continue
+        g = lambda k: m.get(k, float("nan"))  # noqa: E731
+        rd = 32 * g("TCC_EA0_RDREQ_32B_sum") + 64 * g("TCC_EA0_RDREQ_64B_sum") + 128 * g("TCC_EA0_RDREQ_128B_sum")
+        unsized = g("TCC_EA0_RDREQ_sum") - g("TCC_EA0_RDREQ_32B_sum") - g("TCC_EA0_RDREQ_64B_sum") \
+            - g("TCC_EA0_RDREQ_128B_sum")
+        wr = 64 * g("TCC_EA0_WRREQ_64B_sum") + 32 * (g("TCC_EA0_WRREQ_sum") - g("TCC_EA0_WRREQ_64B_sum"))
+        rows.append({"kernel": label, "dispatches": n_disp, "read_bytes": rd, "write_bytes": wr,
+                     "read_requests_without_size": unsized,
+                     "read_requests_to_dram_frac": g("TCC_EA0_RDREQ_DRAM_sum") / g("TCC_EA0_RDREQ_sum"),
+                     "write_requests_to_dram_frac": g("TCC_EA0_WRREQ_DRAM_sum") / g("TCC_EA0_WRREQ_sum"),
+                     "algorithmic_read_bytes": alg_r, "algorithmic_write_bytes": alg_w,
+                     "read_over_algorithmic": rd / alg_r, "write_over_algorithmic": wr / alg_w,
+                     "requests": {k: m[k] for k in sorted(m)}})
+    for r in rows:
+        print(json.dumps(r), flush=True)
 
 
 def emit(d):

@@ -61,3 +61,34 @@ def test_traffic_figure_is_gated_on_the_kernel_source(tmp_path, monkeypatch):
     assert bench.measured_traffic() == 123456789.0
     src.write_text(src.read_text() + "\n// edited\n")
     assert bench.measured_traffic() is None
+
+
+def test_counters_report_prices_requests_by_size(tmp_path, capsys):
+    """--counters-report: bytes = 32/64/128 x the read requests of each size and
+    64 / 32 x the 64-byte / other write requests, per dispatch, beside the
+    algorithmic bytes of the --traffic kernels."""
+    import csv
+    import json
+    w = workloads.WORKLOAD_BY_NAME[bench.TRAFFIC_WORKLOAD]
+    known = {sub: (r, wr) for _, sub, r, wr in bench.traffic_known(w)}
+    counts = {"TCC_EA0_RDREQ_sum": 110.0, "TCC_EA0_RDREQ_32B_sum": 10.0, "TCC_EA0_RDREQ_64B_sum": 20.0,
+              "TCC_EA0_RDREQ_128B_sum": 80.0, "TCC_EA0_WRREQ_sum": 50.0, "TCC_EA0_WRREQ_64B_sum": 40.0,
+              "TCC_EA0_RDREQ_DRAM_sum": 110.0, "TCC_EA0_WRREQ_DRAM_sum": 50.0}
+    f = tmp_path / "run" / "x_counter_collection.csv"
+    f.parent.mkdir()
+    with open(f, "w", newline="") as fh:
+        wr = csv.writer(fh)
+        wr.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for disp in range(2):  # two dispatches of the shard pass; the second doubles every count
+            for k, v in counts.items():
+                wr.writerow([disp, "void ra::fwd_bf16_kernel<128>(FwdParams)", k, v * (1 + disp)])
+    bench.counters_report([str(tmp_path)])
+    rows = [json.loads(line) for line in capsys.readouterr().out.splitlines()]
+    assert len(rows) == 1 and rows[0]["dispatches"] == 2
+    r = rows[0]
+    assert r["read_bytes"] == 1.5 * (10 * 32 + 20 * 64 + 80 * 128)
+    assert r["write_bytes"] == 1.5 * (40 * 64 + 10 * 32)
+    assert r["read_requests_without_size"] == 0
+    assert (r["algorithmic_read_bytes"], r["algorithmic_write_bytes"]) == known["fwd_bf16_kernel"]
+    # Algorithmic bytes of the shard pass: Q of the shard plus K and V of every block, out (bf16) + lse.
+    assert known["fwd_bf16_kernel"] == (33554432 + 2 * 33554432, 33554432 + 524288)
