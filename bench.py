@@ -149,6 +149,10 @@ def main():
                     help="run the kernels whose memory traffic is measured (under rocprofv3 --pmc): a plain "
                          "conversion copy, the shard gather of Q, a two-part merge and the benchmarked shard pass, "
                          f"{TRAFFIC_DISPATCHES} dispatches each")
+    ap.add_argument("--power", action="store_true",
+                    help="board power (hwmon) and rate while one kernel runs back to back for a few seconds: "
+                         "the benchmarked shard pass on the benchmark's inputs and on zero inputs, and a "
+                         "matrix-core stream (libmfma_stream.so) on N(0,1) and on zero operands")
     ap.add_argument("--counters-report", nargs="+", metavar="DIR",
                     help="summarise rocprofv3 counter CSVs under these directories for the --traffic kernels: "
                          "bytes per dispatch from request counts by request size, beside the algorithmic bytes")
@@ -169,6 +173,9 @@ def main():
         return
     if args.traffic:
         traffic_run()
+        return
+    if args.power:
+        power_run()
         return
     w = workloads.WORKLOAD_BY_NAME[args.workload]
     # The CPU baseline runs first, bounded, so that the GPU leg that follows is
@@ -369,6 +376,122 @@ def counters_report(dirs):
                      "requests": {k: m[k] for k in sorted(m)}})
     for r in rows:
         print(json.dumps(r), flush=True)
+
+
+POWER_SECONDS = 3.0
+
+
+def hwmon_power_files():
+    """(power reading, power cap, junction temperature) sysfs files of the
+    GPU's hwmon, or None."""
+    import glob
+    for d in sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*")):
+        for name in ("power1_input", "power1_average"):
+            f = os.path.join(d, name)
+            if os.path.exists(f):
+                temp = None
+                for t in sorted(glob.glob(os.path.join(d, "temp*_label"))):
+                    try:
+                        if open(t).read().strip() == "junction":
+                            temp = t.replace("_label", "_input")
+                    except OSError:
+                        pass
+                return f, os.path.join(d, "power1_cap"), temp
+    return None
+
+
+def power_run():
+    """Board power while one kernel runs back to back for POWER_SECONDS (the
+    reading is sampled every 50 ms by a host thread; the median of the last
+    three quarters is reported), beside the rate the kernel reached."""
+    import ctypes
+    import threading
+    import torch
+    import ring_parallelism_amd as ra
+    files = hwmon_power_files()
+
+    def read_w(f):
+        try:
+            return int(open(f).read().strip()) / 1e6
+        except (OSError, ValueError):
+            return None
+
+    cap = read_w(files[1]) if files else None
+    w = workloads.WORKLOAD_BY_NAME["s128k_c16_zigzag_16x1"]
+    dev = torch.device("cuda:0")
+    c = w.n_shards
+    qs, ks, vs = device_inputs(w, torch, dev, blocks_for=[0])
+    out = torch.empty((w.batch, w.h_q, w.n_loc, w.head_dim), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.batch, w.h_q, w.n_loc), dtype=torch.float32, device=dev)
+    desc = ra.make_desc(w.seq_len, c, w.split, w.batch, w.h_q, w.h_kv, w.head_dim, ra.BF16, ra.BF16, w.causal, w.scale)
+    own = [(0 - t) % c for t in range(c)]
+    zq, zk, zv = torch.zeros_like(qs[0]), torch.zeros_like(ks), torch.zeros_like(vs)
+
+    def shard(q, k, v):
+        return lambda: ra.ring_attn_shard_fwd(desc, 0, q, [k[j] for j in own], [v[j] for j in own], out, lse)
+
+    from ring_parallelism_amd import build as hip_build
+    slib = ctypes.CDLL(hip_build.STREAM_LIB)
+    slib.mfma_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_void_p,
+                                 ctypes.c_void_p]
+    slib.mfma_stream.restype = ctypes.c_int
+    n_wg, iters = 1024, 15000
+    sink = torch.empty((n_wg * 512,), dtype=torch.float32, device=dev)
+
+    def stream(zero):
+        def run():
+            rc = slib.mfma_stream(n_wg, iters, int(zero), 11, sink.data_ptr(),
+                                  ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"mfma_stream failed: hip error {rc}")
+        return run
+
+    shard_flop = useful_flop(w, shard_pairs(w, 0))
+    stream_flop = float(n_wg) * 8 * iters * 16 * 32 * 32 * 16 * 2
+    cases = [("fwd_bf16_kernel, shard 0 of the 131 072-token workload", f"N(0,{w.sigma}^2)", shard(qs[0], ks, vs),
+              shard_flop),
+             ("fwd_bf16_kernel, shard 0 of the 131 072-token workload", "zeros", shard(zq, zk, zv), shard_flop),
+             ("mfma_stream (matrix-core products only, operands in registers)", "N(0,1)", stream(False), stream_flop),
+             ("mfma_stream (matrix-core products only, operands in registers)", "zeros", stream(True), stream_flop)]
+    for kernel, inputs, fn, flop in cases:
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        samples, stop = [], threading.Event()
+
+        temps = []
+
+        def sample():
+            while not stop.is_set():
+                if files:
+                    samples.append(read_w(files[0]))
+                    if files[2]:
+                        temps.append(read_w(files[2]))
+                time.sleep(0.05)
+
+        th = threading.Thread(target=sample)
+        th.start()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        calls = 0
+        while time.perf_counter() - t0 < POWER_SECONDS:
+            for _ in range(8):
+                fn()
+            calls += 8
+            torch.cuda.synchronize()
+        e1.record()
+        torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        ms = e0.elapsed_time(e1) / calls
+        tail = [x for x in samples[len(samples) // 4:] if x is not None]
+        tf = flop / (ms / 1e3) / 1e12
+        emit({"measurement": "power", "kernel": kernel, "inputs": inputs, "calls": calls,
+              "ms_per_call": round(ms, 4), "tflops": round(tf, 1), "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+              "board_power_w_median": float(np.median(tail)) if tail else None, "board_power_cap_w": cap,
+              "power_samples": len(tail), "power_file": files[0] if files else None,
+              "junction_temp_c_max": max((x * 1e3 for x in temps if x is not None), default=None)})
 
 
 def emit(d):

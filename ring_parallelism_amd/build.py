@@ -1,4 +1,6 @@
-"""Compile the HIP sources into ``libring_attn.so`` next to this file (gfx950)."""
+"""Compile the HIP sources into ``libring_attn.so`` next to this file (gfx950),
+and the measurement aid ``mfma_stream.hip`` into ``libmfma_stream.so`` (a
+separate library: it is no part of the attention ABI)."""
 from __future__ import annotations
 
 import concurrent.futures
@@ -11,6 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libring_attn.so")
 SOURCES = ["api.cpp", "partition.hip", "fwd_f32.hip", "fwd_bf16.hip", "merge.hip", "decode.hip", "noalloc.hip"]
+STREAM_LIB = os.path.join(HERE, "libmfma_stream.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -50,5 +53,19 @@ def build(out: str = LIB, extra: list | None = None, verbose: bool = False) -> s
     return out
 
 
+def build_stream(out: str = STREAM_LIB, verbose: bool = False) -> str:
+    """The matrix-core stream used by bench.py --power."""
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-shared", "-Wl,--no-undefined", os.path.join(CSRC, "mfma_stream.hip"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for mfma_stream.hip:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, out)
+    if verbose:
+        print(f"built {out}")
+    return out
+
+
 if __name__ == "__main__":
     build(extra=sys.argv[1:], verbose=True)
+    build_stream(verbose=True)
