@@ -92,3 +92,15 @@ def test_counters_report_prices_requests_by_size(tmp_path, capsys):
     assert (r["algorithmic_read_bytes"], r["algorithmic_write_bytes"]) == known["fwd_bf16_kernel"]
     # Algorithmic bytes of the shard pass: Q of the shard plus K and V of every block, out (bf16) + lse.
     assert known["fwd_bf16_kernel"] == (33554432 + 2 * 33554432, 33554432 + 524288)
+
+
+def test_matrix_core_stream_is_outside_the_attention_library():
+    """The measurement aid behind bench.py --power lives in its own library:
+    the attention library exports no such symbol."""
+    import ctypes
+    from ring_parallelism_amd import build as hip_build
+    import ring_parallelism_amd as ra
+    if not os.path.exists(hip_build.STREAM_LIB):
+        hip_build.build_stream()
+    assert hasattr(ctypes.CDLL(hip_build.STREAM_LIB), "mfma_stream")
+    assert not hasattr(ra.lib(), "mfma_stream")
