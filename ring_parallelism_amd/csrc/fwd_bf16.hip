@@ -269,9 +269,11 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
 
     // Tile iterator over (block t, key tile kt), skipping blocks with no
     // visible key.  A state is (t, kt, n_vis, n_full); t >= t1: done.
-    // The cursor also carries the block's K and V base addresses, read from
-    // the argument block once per block: a scalar load in the per-tile path
-    // would make every tile wait for all of the wave's LDS reads as well.
+    // The cursor of the tile loads also carries the block's K and V base
+    // addresses, read from the argument block once per block (a scalar load
+    // in the per-tile path would make every tile wait for all of the wave's
+    // LDS reads as well); the counting pass and the masking cursor need only
+    // the counts and read no address.
     struct Tile {
       int t, kt, vis, full;
       const __bf16* kb;
@@ -279,20 +281,25 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
     };
     auto block_counts = [&](Tile& x) {
       const int j = owner_of(x.t);
-      x.kb = (const __bf16*)block_k(x.t) + kv_off;
-      x.vb = (const __bf16*)block_v(x.t) + kv_off;
       const int c_last = p.causal ? count_upto32(j, pos_last, n_loc, p.c, p.split) : n_loc;
       const int c_first = p.causal ? count_upto32(j, pos_first, n_loc, p.c, p.split) : n_loc;
       x.vis = (c_last + kBK - 1) / kBK;
       x.full = rows_full ? c_first / kBK : 0;
     };
-    auto advance = [&](Tile x) {
+    auto block_addrs = [&](Tile& x) {
+      x.kb = (const __bf16*)block_k(x.t) + kv_off;
+      x.vb = (const __bf16*)block_v(x.t) + kv_off;
+    };
+    auto advance = [&](Tile x, auto WithAddrs) {
       if (x.t >= t1) return x;
       if (++x.kt < x.vis) return x;
       x.kt = 0;
       while (++x.t < t1) {
         block_counts(x);
         if (x.vis > 0) break;
+      }
+      if constexpr (decltype(WithAddrs)::value != 0) {
+        if (x.t < t1) block_addrs(x);
       }
       return x;
     };
@@ -537,6 +544,7 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
         x.t = t;
         x.kt = 0;
         block_counts(x);
+        if (x.vis > 0) block_addrs(x);
         for (int kt = 0; kt < x.vis; ++kt) {
           x.kt = kt;
           __syncthreads();  // every wave has finished reading stage 0
@@ -574,6 +582,7 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
       if (x.vis > 0 && first.t < 0) first = x;
       n_tiles += x.vis;
     }
+    if (first.t >= 0) block_addrs(first);
     // Every row of the query tile sees key 0 of the first tile (so that the
     // first tile gives every row a finite reference) unless a causal mask
     // hides it from the tile's first row (positions ascend).
@@ -583,7 +592,7 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
       Tile ld = first;
       static_for<0, C::AHEAD>([&](auto I) {
         if (decltype(I)::value < n_tiles) issue_loads(I, ld);
-        ld = advance(ld);
+        ld = advance(ld, Ic<1>{});
       });
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
@@ -604,7 +613,7 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
       // straight-line block for the scheduler.  Returns false after the last
       // tile.
       int i = 0;
-      Tile nx = advance(first);  // tile i+1
+      Tile nx = advance(first, Ic<0>{});  // tile i+1
       auto step = [&](auto K) {
         constexpr int k = decltype(K)::value;
         auto& x = (k % 2 == 0) ? xa : xb;
@@ -615,7 +624,7 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
           static_for<0, G>([&](auto J) {
             constexpr int jx = decltype(J)::value;
             if (i + C::AHEAD + jx < n_tiles) issue_loads(Ic<(k + C::AHEAD + jx) % NS>{}, ld);
-            ld = advance(ld);
+            ld = advance(ld, Ic<1>{});
           });
           // Measurement mode: no overlap of the tile transfers with compute.
           if (p.sync_loads) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -666,7 +675,7 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
         }
         if (++i >= n_tiles) return false;
         if (nx.kt >= nx.full) mask(y, nx);  // tile i (the next step's x)
-        nx = advance(nx);
+        nx = advance(nx, Ic<0>{});
         return true;
       };
       // Stages rotate with period NS, the score buffers with period 2 and
