@@ -41,8 +41,8 @@ def cpu_baseline(w, target_s):
     """The fp64 oracle on a bounded row sample of shard 0, one query head at a time."""
     import oracle
     q_pos_all = oracle.partition_perm(w.seq_len, w.n_shards, w.split)[:w.n_loc]
-    # Rows in a seeded random order so the sample's mix of early and late
-    # tokens matches the shard's; heads 0, 1, ... in turn.
+    # Rows in a seeded random order so that the sample's spread of early and
+    # late tokens is the shard's; heads 0, 1, ... in turn.
     order = np.random.default_rng(0).permutation(w.n_loc)
     k = workloads.draw(w.seed, workloads.TENSOR_K, w.batch, w.h_kv, w.seq_len, w.head_dim, w.sigma, w.dtype)
     v = workloads.draw(w.seed, workloads.TENSOR_V, w.batch, w.h_kv, w.seq_len, w.head_dim, w.sigma, w.dtype)

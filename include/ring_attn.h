@@ -13,9 +13,10 @@
  *   - Every function returns ra_status; RA_OK (0) on success.  On failure
  *     nothing was launched and ring_attn_last_error() describes the cause.
  *   - Device buffers are owned by the caller; the library allocates no
- *     device memory, keeps no state between calls and is thread-safe.  Host
- *     arrays passed in (block_owner, k_blocks, v_blocks, outs, lses) are read
- *     during the call only.
+ *     device memory and is thread-safe.  Its only device state is the static
+ *     scratch of ring_attn_shard_fwd_split_noalloc (see there).  Host arrays
+ *     passed in (block_owner, k_blocks, v_blocks, outs, lses) are read during
+ *     the call only.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     on it and the call returns at once; faults surface at the caller's next
  *     synchronisation.
@@ -74,12 +75,13 @@ typedef struct {
   uint32_t flags;    /* RA_FLAG_* bits; 0 for normal use */
 } ra_attn_desc;
 
-/* Measurement switch for the "with and without overlap" comparison
- * ("Sequence / context parallelism" notes, section 10, exercise C): the
- * key/value tiles are still prefetched into the LDS ring, but every wave
- * waits for each batch of tile loads right after issuing it, so the transfer
- * no longer overlaps the attention arithmetic.  Results are bitwise the same.
- * bf16 inputs only (RA_EUNSUPPORTED with fp32 inputs). */
+/* Measurement switch for timing the pass with its block transfers hidden
+ * behind the arithmetic and without ("Sequence / context parallelism" notes,
+ * section 10, exercise C): the key/value tiles are still prefetched into the
+ * LDS ring, but every wave waits for each batch of tile loads right after
+ * issuing it, so no transfer runs beside the attention arithmetic.  Results
+ * are bitwise the same.  bf16 inputs only (RA_EUNSUPPORTED with fp32
+ * inputs). */
 #define RA_FLAG_SYNC_LOADS 1u
 
 /* q, out and lse are the natural-order, full-sequence tensors [B, h_q, S, d]
@@ -104,7 +106,11 @@ typedef struct {
 #define RA_FLAG_EVENT_COUNTS 4u
 #define RA_STATS_EVENTS_LEN 6
 
-/* Shard placement and optional gather into shard-major order.
+/* Shard placement and optional gather into shard-major order: which
+ * tokens each device of the ring holds ("Splitting the Sequence", intro and
+ * Terms: the zig-zag split of 2c chunks; "Sequence / context parallelism"
+ * notes, section 1 for contiguous shards and section 5 for the interleaved
+ * and zig-zag placements that balance the causal work).
  *
  * perm (device int64[S], may be NULL): perm[r*(S/c) + t] = global position
  *   of shard r's t-th token under `split`.
@@ -121,14 +127,21 @@ ra_status zigzag_partition(int64_t seq_len, int32_t n_shards, int32_t split, int
                            const void* src, void* dst, int64_t outer, int64_t inner_bytes,
                            void* stream);
 
-/* The inverse placement: scatter shard-major rows back to natural order.
+/* The inverse placement: scatter shard-major rows back to natural order
+ * (the output of a sequence-parallel layer returned to token order; same
+ * passages as zigzag_partition).
  * src viewed as [c][outer][S/c][inner_bytes], dst as [outer][S][inner_bytes];
  * dst[o][perm[r*(S/c)+t]] = src[r][o][t].  Same errors as zigzag_partition. */
 ra_status zigzag_unpartition(int64_t seq_len, int32_t n_shards, int32_t split,
                              const void* src, void* dst, int64_t outer, int64_t inner_bytes,
                              void* stream);
 
-/* One shard's queries against a sequence of key/value blocks.
+/* One shard's queries against a sequence of key/value blocks: the ring
+ * pass of one device, its queries kept in place while the blocks arrive in
+ * ring order, each folded in by the online softmax ("Sequence / context
+ * parallelism" notes, section 4 "Ring Attention -- the core algorithm";
+ * "Splitting the Sequence", intro; "Sequence Parallelism and Ring Attention
+ * Quiz", Q2-Q4 and Q7).
  *
  * rank         : the shard r in [0, c) whose queries q holds.
  * q            : device [B, h_q, S/c, d] in_dtype, shard r's tokens in shard order
@@ -189,7 +202,10 @@ ra_status ring_attn_all_shards_fwd(const ra_attn_desc* desc, const void* q_shard
                                    void* out_shards, float* lse_shards, int64_t* stats, void* stream);
 
 /* Tile shape (query rows, keys) that ring_attn_shard_fwd uses for `desc`,
- * i.e. the unit its stats count.  Errors as for the descriptor checks. */
+ * i.e. the unit its stats count (the work accounting behind the balance
+ * comparison of causal placements: "Splitting the Sequence", "One sequence,
+ * sixteen devices", the busiest device's share of the work under the
+ * contiguous split).  Errors as for the descriptor checks. */
 ra_status ring_attn_tile_shape(const ra_attn_desc* desc, int32_t* tile_q, int32_t* tile_k);
 
 /* n-way merge of partial results over disjoint key sets.
@@ -254,7 +270,9 @@ ra_status ring_attn_shard_fwd_split_noalloc(const ra_attn_desc* desc, int32_t ra
                                             int32_t n_splits, void* out, float* lse, int64_t* stats,
                                             void* stream);
 
-/* ring_attn_merge with the parts in one buffer: part k's out starts
+/* ring_attn_merge with the parts in one buffer (the same fold, "Sequence /
+ * context parallelism" notes, section 4; also the gather of decode partials,
+ * section 7): part k's out starts
  * out_stride elements after part k-1's (parts_dtype elements, out_stride >=
  * batch*heads*rows*head_dim) and its lse lse_stride values after part k-1's
  * (lse_stride >= batch*heads*rows).  Any n_parts >= 1.  out / lse may be part
@@ -289,10 +307,11 @@ ra_status ring_attn_decode(const ra_attn_desc* desc, const void* q, int32_t n_bl
                            const void* const* k_blocks, const void* const* v_blocks, int32_t n_splits,
                            float* out_parts, float* lse_parts, void* stream);
 
-/* Message for the last non-OK status returned on this thread. */
+/* Message for the last non-OK status returned on this thread (interface
+ * plumbing; no passage of the method). */
 const char* ring_attn_last_error(void);
 
-/* RA_ABI_VERSION of the loaded library. */
+/* RA_ABI_VERSION of the loaded library (interface plumbing). */
 int32_t ring_attn_abi_version(void);
 
 #ifdef __cplusplus

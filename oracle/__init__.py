@@ -155,8 +155,8 @@ def shard_positions(seq_len: int, n_shards: int, split: int, rank: int) -> np.nd
 
 # ---------------------------------------------------------------------------
 # Work accounting.  Under the causal mask a query at position i sees i+1 keys
-# ("Sequence Parallelism and Ring Attention Quiz", Q6 and Q8: later tokens
-# attend to more keys), so the work of a shard is the number of visible
+# ("Sequence Parallelism and Ring Attention Quiz", Q6 and Q8: the later a
+# token stands, the more keys it sees), so the work of a shard is the number of visible
 # (query, key) pairs of its tokens ("Splitting the Sequence", "One sequence,
 # sixteen devices": busiest device versus the average).
 # ---------------------------------------------------------------------------

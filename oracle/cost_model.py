@@ -17,13 +17,14 @@ printed figure in ``tests/test_cost_model.py``):
   tokens times hidden size, divided by the tensor-parallel degree t (their
   sequence-parallel form) and by the context-parallel degree c; a pipeline
   stage holds layers / p of the layers.
-* The ring sends, per layer, this device's share of the bf16 keys and
-  values over the whole sequence (its n_kv / t heads), (c - 1)/c of it
-  leaving the device, over one link of the stated rate.
-* Attention compute per layer per device is the causal forward work of the
-  busiest device (all equal under the zig-zag split): 4 * d FLOP per visible
-  (query, key) pair and query head, run at a fraction of the peak.
-* "H100 peak" is the dense bf16 figure of the SXM part, 989.4 TFLOP/s.
+* Per layer, the ring moves the bf16 keys and values of the device's own
+  n_kv / t heads over the whole sequence; the fraction (c - 1)/c of those
+  bytes leaves the device, over one link of the stated rate.
+* The attention arithmetic of a layer on one device is the causal forward
+  work of the busiest device (all equal under the zig-zag split): 4 * d FLOP
+  per visible (query, key) pair and query head, run at a fraction of the
+  peak.
+* The H100 peak is the dense bf16 figure of the SXM part, 989.4 TFLOP/s.
 """
 from __future__ import annotations
 
