@@ -279,12 +279,32 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
       const __bf16* kb;
       const __bf16* vb;
     };
+    // Per-block tile counts of this query tile, in lanes: lane u of
+    // register h holds block 64h + u's visible and full key-tile counts (0
+    // outside [t0, t1)).  Computed once per query tile on the vector unit --
+    // every wave would otherwise repeat the same scalar arithmetic on the
+    // compute unit's one scalar unit -- and read by a cursor entering a
+    // block with one v_readlane.
+    int lvis[2], lfull[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      lvis[h] = 0;
+      lfull[h] = 0;
+      if (h == 0 || t1 > 64) {
+        const int t = 64 * h + lane;
+        if (t >= t0 && t < t1) {
+          const int j = p.all_ranks ? ring_owner(t) : p.owner[t];
+          const int c_last = p.causal ? count_upto32(j, pos_last, n_loc, p.c, p.split) : n_loc;
+          const int c_first = p.causal ? count_upto32(j, pos_first, n_loc, p.c, p.split) : n_loc;
+          lvis[h] = (c_last + kBK - 1) / kBK;
+          lfull[h] = rows_full ? c_first / kBK : 0;
+        }
+      }
+    }
     auto block_counts = [&](Tile& x) {
-      const int j = owner_of(x.t);
-      const int c_last = p.causal ? count_upto32(j, pos_last, n_loc, p.c, p.split) : n_loc;
-      const int c_first = p.causal ? count_upto32(j, pos_first, n_loc, p.c, p.split) : n_loc;
-      x.vis = (c_last + kBK - 1) / kBK;
-      x.full = rows_full ? c_first / kBK : 0;
+      const int u = x.t & 63;
+      x.vis = x.t < 64 ? __builtin_amdgcn_readlane(lvis[0], u) : __builtin_amdgcn_readlane(lvis[1], u);
+      x.full = x.t < 64 ? __builtin_amdgcn_readlane(lfull[0], u) : __builtin_amdgcn_readlane(lfull[1], u);
     };
     auto block_addrs = [&](Tile& x) {
       x.kb = (const __bf16*)block_k(x.t) + kv_off;
@@ -573,16 +593,20 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
     first.vis = 0;
     first.full = 0;
     first.kb = first.vb = nullptr;
-    int n_tiles = 0;
-    for (int t = t0; t < t1; ++t) {
-      Tile x;
-      x.t = t;
-      x.kt = 0;
-      block_counts(x);
-      if (x.vis > 0 && first.t < 0) first = x;
-      n_tiles += x.vis;
+    int n_tiles;
+    {
+      int tot = lvis[0] + lvis[1];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off);
+      n_tiles = __builtin_amdgcn_readfirstlane(tot);
+      const uint64_t m0 = __builtin_amdgcn_ballot_w64(lvis[0] > 0);
+      const uint64_t m1 = __builtin_amdgcn_ballot_w64(lvis[1] > 0);
+      if (m0 | m1) {
+        first.t = m0 ? (int)__builtin_ctzll(m0) : 64 + (int)__builtin_ctzll(m1);
+        block_counts(first);
+        block_addrs(first);
+      }
     }
-    if (first.t >= 0) block_addrs(first);
     // Every row of the query tile sees key 0 of the first tile (so that the
     // first tile gives every row a finite reference) unless a causal mask
     // hides it from the tile's first row (positions ascend).
