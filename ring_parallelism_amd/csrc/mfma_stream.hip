@@ -45,6 +45,8 @@ __device__ inline float unit_normal(uint32_t& state) {
 __global__ __launch_bounds__(kThreads) void mfma_stream_kernel(int iters, int zero_operands, uint32_t seed,
                                                                 float* __restrict__ out) {
   const uint32_t tid = blockIdx.x * kThreads + threadIdx.x;
+  // Per-thread start: Knuth's multiplicative hash of the thread id (the
+  // golden-ratio multiplier, The Art of Computer Programming vol. 3, 6.4).
   uint32_t state = (tid + 1u) * 2654435761u ^ seed;
   state = state ? state : 1u;  // xorshift32 never leaves a nonzero state, never reaches one from zero
   bf16x8 a[4], b[4];
