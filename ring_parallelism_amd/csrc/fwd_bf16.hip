@@ -37,10 +37,12 @@
 // (every G steps) a row whose lane sum l has passed 2^32 -- some scores rose
 // more than 32 log2 units above m -- raises m by the integer part of log2 l
 // and rescales O and l by that exact power of two.  Between two checks a
-// score would have to jump more than 96 log2 units above every earlier one
-// to overflow; if that happens (or a row of the first tile sees no key, as
-// some block orders allow), the query tile is recomputed from scratch by the
-// plain per-tile online softmax (exact tile max, rescale whenever it rises).
+// score would have to jump roughly 90 log2 units or more above every earlier
+// one for fp32 to overflow (an exponential, the row sum or the output); if
+// that happens -- seen as a non-finite sum or output after the pass -- or a
+// row of the first tile sees no key, as some block orders allow, the query
+// tile is recomputed from scratch by the plain per-tile online softmax (exact
+// tile max, rescale whenever it rises).
 //
 // Workgroup: NW wavefronts x NB 32-row blocks = BQ query rows of one
 // (batch, head).  Each workgroup takes query tiles p and n_qtiles-1-p of the
@@ -50,8 +52,10 @@
 // Consecutive workgroup ids are placed on one XCD, so the query heads that
 // share a key/value head stream the same K/V through one L2.  The grid may
 // also be split over groups of blocks (each group writes a partial result to
-// be merged), and q / out / lse may be addressed at global token positions of
-// natural-order tensors instead of shard order.
+// be merged), q / out / lse may be addressed at global token positions of
+// natural-order tensors instead of shard order, and every rank's pass may run
+// in one launch (the rank taken from the work index, each XCD given a slice
+// of every rank).
 #include <type_traits>
 
 #include "ra_common.h"

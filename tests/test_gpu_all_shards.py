@@ -28,6 +28,10 @@ CASES = [
     # rank first) rather than whole ranks.
     (4096, 4, ra.SPLIT_CONTIGUOUS, 1, 8, 2, 128, "bf16", True),
     (4096, 4, ra.SPLIT_ZIGZAG, 2, 4, 4, 128, "bf16", True),
+    # More than 64 ranks: blocks 64 and up take the second lane register of
+    # the kernel's per-block count table.
+    (12800, 100, ra.SPLIT_CONTIGUOUS, 1, 2, 1, 128, "bf16", True),
+    (12800, 100, ra.SPLIT_STRIPED, 1, 2, 1, 64, "bf16", True),
 ]
 
 

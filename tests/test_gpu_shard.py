@@ -164,10 +164,11 @@ def test_split_pass_matches_oracle_and_counts(S, c, split, B, Hq, Hkv, d, n_spli
         assert torch.equal(stats, s1), f"stats rank {r}"
 
 
-@pytest.mark.parametrize("split", [ra.SPLIT_ZIGZAG, ra.SPLIT_CONTIGUOUS])
+@pytest.mark.parametrize("split", [ra.SPLIT_ZIGZAG, ra.SPLIT_CONTIGUOUS, ra.SPLIT_STRIPED])
 def test_maximum_block_count(split):
     """RA_MAX_BLOCKS (128) ring blocks in one call: every row of three ranks,
-    and the work counters."""
+    and the work counters (blocks 64-127 take the second lane register of
+    the kernel's per-block count table)."""
     S, c = 16384, 128
     p = Problem(S, c, split, 1, 2, 1, 128, "bf16", seed=77)
     tq, tk = ra.ring_attn_tile_shape(p.desc())
