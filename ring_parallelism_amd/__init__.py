@@ -23,6 +23,8 @@ FLAG_EVENT_COUNTS = 4
 STATS_EVENTS_LEN = 6
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 MAX_BLOCKS = 128
+NOALLOC_MAX_PARTIAL_FLOATS = 1 << 24  # static scratch of ring_attn_shard_fwd_split_noalloc
+NOALLOC_MAX_LSE_FLOATS = 1 << 17
 MAX_PARTS = 64
 
 # RING_ATTN_LIB may name another build of the same library (tuning variants).

@@ -259,3 +259,40 @@ def test_shard_fwd_split_validation():
     expect(ra.EINVAL, f, good_desc(), 0, FAKE, kb, kb, 2, W + 8, W, FAKE, FAKE, match="aligned")
     expect(ra.EINVAL, f, good_desc(), 0, FAKE, kb, kb, 2, W, W * 2, W + 16, FAKE, match="overlaps")
     expect(ra.EINVAL, f, good_desc(), 9, FAKE, kb, kb, 2, W, W, FAKE, FAKE, match="rank")
+
+
+def test_noalloc_split_validation_before_any_device_call():
+    """ring_attn_shard_fwd_split_noalloc rejects a call whose partials exceed
+    its static scratch (2^24 floats of partial output) before touching the
+    device, and reports the split pass's own argument errors."""
+    assert ra.NOALLOC_MAX_PARTIAL_FLOATS == 1 << 24 and ra.NOALLOC_MAX_LSE_FLOATS == 1 << 17
+    # 8 192 tokens, c = 8, 32 / 8 heads: 4 groups fill the scratch exactly, 8 do not fit.
+    d = good_desc(seq_len=8192, n_shards=8, h_q=32, h_kv=8)
+    kb = [FAKE] * 8
+    expect(ra.EINVAL, ra.ring_attn_shard_fwd_split_noalloc, d, 0, FAKE, kb, kb, 8, FAKE, FAKE, match="static scratch")
+    expect(ra.EINVAL, ra.ring_attn_shard_fwd_split_noalloc, d, 0, FAKE, kb, kb, 0, FAKE, FAKE, match="n_splits")
+    expect(ra.EINVAL, ra.ring_attn_shard_fwd_split_noalloc, good_desc(seq_len=0), 0, FAKE, kb[:4], kb[:4], 2,
+           FAKE, FAKE, match="seq_len")
+
+
+def test_binding_constants_match_the_header():
+    """Every #define and enum value the binding mirrors equals the header's."""
+    text = open(HEADER).read()
+    def value(expr):  # "4u", "128", "1 << 24"
+        parts = [int(x) for x in expr.replace("u", "").split("<<")]
+        return parts[0] << parts[1] if len(parts) == 2 else parts[0]
+
+    defs = {m.group(1): value(m.group(2))
+            for m in re.finditer(r"#define (RA_\w+) \(?([0-9][0-9 <]*u?)\)?", text)}
+    assert defs["RA_FLAG_SYNC_LOADS"] == ra.FLAG_SYNC_LOADS
+    assert defs["RA_FLAG_NATURAL_QO"] == ra.FLAG_NATURAL_QO
+    assert defs["RA_FLAG_EVENT_COUNTS"] == ra.FLAG_EVENT_COUNTS
+    assert defs["RA_STATS_EVENTS_LEN"] == ra.STATS_EVENTS_LEN
+    assert defs["RA_MAX_BLOCKS"] == ra.MAX_BLOCKS and defs["RA_MAX_PARTS"] == ra.MAX_PARTS
+    assert defs["RA_NOALLOC_MAX_PARTIAL_FLOATS"] == ra.NOALLOC_MAX_PARTIAL_FLOATS
+    assert defs["RA_NOALLOC_MAX_LSE_FLOATS"] == ra.NOALLOC_MAX_LSE_FLOATS
+    enums = dict(re.findall(r"(RA_\w+) = (\d+)", text))
+    assert (int(enums["RA_OK"]), int(enums["RA_EINVAL"]), int(enums["RA_EUNSUPPORTED"]), int(enums["RA_EHIP"])) == \
+        (ra.OK, ra.EINVAL, ra.EUNSUPPORTED, ra.EHIP)
+    assert (int(enums["RA_SPLIT_ZIGZAG"]), int(enums["RA_SPLIT_STRIPED"])) == (ra.SPLIT_ZIGZAG, ra.SPLIT_STRIPED)
+    assert (int(enums["RA_F32"]), int(enums["RA_BF16"])) == (ra.F32, ra.BF16)
