@@ -11,6 +11,7 @@
 // race on it.  Nothing in it needs clearing: each call overwrites every
 // partial row (out and lse) before the merge reads it.
 #include <atomic>
+#include <cstdint>
 
 #include "ra_common.h"
 
@@ -54,9 +55,15 @@ extern "C" ra_status ring_attn_shard_fwd_split_noalloc(const ra_attn_desc* desc,
   if (desc->seq_len < 1 || desc->n_shards < 1 || desc->batch < 1 || desc->h_q < 1 || n_splits < 1)
     return ring_attn_shard_fwd_split(desc, rank, q, n_blocks, block_owner, k_blocks, v_blocks, n_splits, nullptr,
                                      nullptr, out, lse, stats, stream);  // reports the argument error
-  const int64_t rows = (int64_t)desc->batch * desc->h_q * (desc->seq_len / desc->n_shards);
-  const int64_t out_floats = (int64_t)n_splits * rows * desc->head_dim;
-  const int64_t lse_floats = (int64_t)n_splits * rows;
+  // Products saturate instead of wrapping, so no descriptor slips past the
+  // size check by overflow.
+  auto mul = [](int64_t a, int64_t b) {
+    int64_t r;
+    return __builtin_mul_overflow(a, b, &r) ? INT64_MAX : r;
+  };
+  const int64_t rows = mul(mul(desc->batch, desc->h_q), desc->seq_len / desc->n_shards);
+  const int64_t lse_floats = mul(n_splits, rows);
+  const int64_t out_floats = mul(lse_floats, desc->head_dim);
   if (out_floats > kScratchOutFloats || lse_floats > kScratchLseFloats)
     return ra::set_error(RA_EINVAL,
                          "n_splits * batch * h_q * S/c * head_dim = %lld floats exceeds the static scratch "

@@ -296,3 +296,10 @@ def test_binding_constants_match_the_header():
         (ra.OK, ra.EINVAL, ra.EUNSUPPORTED, ra.EHIP)
     assert (int(enums["RA_SPLIT_ZIGZAG"]), int(enums["RA_SPLIT_STRIPED"])) == (ra.SPLIT_ZIGZAG, ra.SPLIT_STRIPED)
     assert (int(enums["RA_F32"]), int(enums["RA_BF16"])) == (ra.F32, ra.BF16)
+
+
+def test_noalloc_size_check_does_not_wrap():
+    """Sizes whose product overflows 64 bits are still rejected by the size check."""
+    d = good_desc(seq_len=(1 << 30), n_shards=2, batch=1 << 20, h_q=1 << 20, h_kv=1 << 20)
+    kb = [FAKE] * 2
+    expect(ra.EINVAL, ra.ring_attn_shard_fwd_split_noalloc, d, 0, FAKE, kb, kb, 2, FAKE, FAKE, match="static scratch")
