@@ -55,6 +55,12 @@ ra_status check_split(int64_t S, int32_t c, int32_t split) {
   return RA_OK;
 }
 
+// a * b, or INT64_MAX where that overflows (size checks must not wrap).
+int64_t mul_sat(int64_t a, int64_t b) {
+  int64_t r;
+  return __builtin_mul_overflow(a, b, &r) ? INT64_MAX : r;
+}
+
 ra_status check_desc(const ra_attn_desc* d) {
   if (!d) return fail(RA_EINVAL, "desc is NULL");
   ra_status st = check_split(d->seq_len, d->n_shards, d->split);
@@ -83,7 +89,7 @@ ra_status check_desc(const ra_attn_desc* d) {
   const int64_t n_loc = d->seq_len / d->n_shards;
   if (n_loc * d->head_dim >= ((int64_t)1 << 31))
     return fail(RA_EUNSUPPORTED, "seq_len/n_shards * head_dim must be < 2^31");
-  if ((int64_t)d->batch * d->h_q * n_loc >= ((int64_t)1 << 40))
+  if (mul_sat(mul_sat(d->batch, d->h_q), n_loc) >= ((int64_t)1 << 40))
     return fail(RA_EUNSUPPORTED, "batch * h_q * seq_len/n_shards too large");
   return RA_OK;
 }

@@ -303,3 +303,9 @@ def test_noalloc_size_check_does_not_wrap():
     d = good_desc(seq_len=(1 << 30), n_shards=2, batch=1 << 20, h_q=1 << 20, h_kv=1 << 20)
     kb = [FAKE] * 2
     expect(ra.EINVAL, ra.ring_attn_shard_fwd_split_noalloc, d, 0, FAKE, kb, kb, 2, FAKE, FAKE, match="static scratch")
+
+
+def test_descriptor_size_bound_does_not_wrap():
+    """batch * h_q * S/c beyond 2^40 is refused even where the product overflows 64 bits."""
+    expect(ra.EUNSUPPORTED, ra.ring_attn_tile_shape, good_desc(seq_len=1 << 24, n_shards=2, batch=1 << 30,
+                                                               h_q=1 << 30, h_kv=1 << 30), match="too large")
