@@ -334,9 +334,8 @@ ra_status ring_attn_merge(int32_t batch, int32_t heads, int64_t rows, int32_t he
     return fail(RA_EINVAL, "unknown dtype");
   if (head_dim % 4 != 0 || 256 % head_dim != 0)
     return fail(RA_EUNSUPPORTED, "head_dim %d must be a multiple of 4 dividing 256", head_dim);
-  const int64_t n_rows = (int64_t)batch * heads * rows;
-  if (n_rows / rows != (int64_t)batch * heads || n_rows > ((int64_t)1 << 40))
-    return fail(RA_EINVAL, "batch * heads * rows too large");
+  const int64_t n_rows = mul_sat(mul_sat(batch, heads), rows);
+  if (n_rows > ((int64_t)1 << 40)) return fail(RA_EINVAL, "batch * heads * rows too large");
   if (!outs || !lses || !out || !lse) return fail(RA_EINVAL, "outs, lses, out and lse must be set");
   const uintptr_t oa = parts_dtype == RA_F32 ? 16 : 8;
   const uintptr_t wa = out_dtype == RA_F32 ? 16 : 8;
@@ -377,9 +376,8 @@ ra_status ring_attn_merge_strided(int32_t batch, int32_t heads, int64_t rows, in
     return fail(RA_EINVAL, "unknown dtype");
   if (head_dim % 4 != 0 || 256 % head_dim != 0)
     return fail(RA_EUNSUPPORTED, "head_dim %d must be a multiple of 4 dividing 256", head_dim);
-  const int64_t n_rows = (int64_t)batch * heads * rows;
-  if (n_rows / rows != (int64_t)batch * heads || n_rows > ((int64_t)1 << 40))
-    return fail(RA_EINVAL, "batch * heads * rows too large");
+  const int64_t n_rows = mul_sat(mul_sat(batch, heads), rows);
+  if (n_rows > ((int64_t)1 << 40)) return fail(RA_EINVAL, "batch * heads * rows too large");
   if (!outs || !lses || !out || !lse) return fail(RA_EINVAL, "outs, lses, out and lse must be set");
   if (out_stride < n_rows * head_dim || lse_stride < n_rows)
     return fail(RA_EINVAL, "strides must be at least one part (%lld elements / %lld lse values)",
@@ -437,7 +435,7 @@ ra_status ring_attn_decode(const ra_attn_desc* desc, const void* q, int32_t n_bl
     return fail(RA_EINVAL, "q, k_blocks, v_blocks, out_parts and lse_parts must be set");
   if (!aligned(q, 16) || !aligned(out_parts, 16) || !aligned(lse_parts, 4))
     return fail(RA_EINVAL, "q / out_parts must be 16-byte aligned, lse_parts 4-byte");
-  const int64_t items = (int64_t)n_blocks * n_splits * desc->batch * desc->h_kv;
+  const int64_t items = mul_sat(mul_sat(mul_sat(n_blocks, n_splits), desc->batch), desc->h_kv);
   if (items >= ((int64_t)1 << 31)) return fail(RA_EUNSUPPORTED, "too many (block, range, batch, kv head) items");
   ra::DecodeParams p;
   std::memset(&p, 0, sizeof p);

@@ -309,3 +309,10 @@ def test_descriptor_size_bound_does_not_wrap():
     """batch * h_q * S/c beyond 2^40 is refused even where the product overflows 64 bits."""
     expect(ra.EUNSUPPORTED, ra.ring_attn_tile_shape, good_desc(seq_len=1 << 24, n_shards=2, batch=1 << 30,
                                                                h_q=1 << 30, h_kv=1 << 30), match="too large")
+
+
+def test_merge_size_bound_does_not_wrap():
+    """batch * heads * rows past 2^40 is refused even where the product overflows 64 bits."""
+    o, l = [FAKE, FAKE * 2], [FAKE * 3, FAKE * 4]
+    expect(ra.EINVAL, ra.ring_attn_merge, 1 << 30, 1 << 30, 1 << 40, 128, o, ra.F32, l, FAKE * 5, ra.F32, FAKE * 6,
+           match="too large")
