@@ -67,10 +67,10 @@
 #define RA_FWD_NW 8
 #endif
 #ifndef RA_FWD_STAGES
-#define RA_FWD_STAGES 8
+#define RA_FWD_STAGES 10
 #endif
 #ifndef RA_FWD_GROUP
-#define RA_FWD_GROUP 2
+#define RA_FWD_GROUP 4
 #endif
 #ifndef RA_FWD_WPE
 #define RA_FWD_WPE 1
@@ -109,7 +109,15 @@ struct Cfg {
   // Tiles of a group's loads that the next group does not read yet (they may
   // stay in flight across its closing barrier), and the matching vmcnt.
   static constexpr int LATE = (AHEAD - G - 2) < G ? (AHEAD - G - 2) : G;
-  static_assert(STAGES * TILEB <= 65536, "stage offsets must fit the 16-bit LDS immediate");
+  // LDS reads name their stage by the instruction's 16-bit immediate; a ring
+  // longer than 64 KiB addresses its later stages from a second base 64 KiB
+  // higher (a tile never straddles the boundary: 64 KiB is a whole number of
+  // tiles).
+  static_assert(65536 % TILEB == 0 && STAGES * TILEB <= 2 * 65536, "stage offsets");
+  static_assert(2 * STAGES * TILEB <= 160 * 1024, "the ring must fit the 160 KiB of LDS");
+  static_assert(NW * 4 <= TILEB, "the per-wave votes live in the last K stage");
+  template <int S> static constexpr uint32_t stage_hi = (uint32_t)(S * TILEB) & ~0xffffu;
+  template <int S> static constexpr int stage_lo = (S * TILEB) & 0xffff;
   static constexpr int RPI = 1024 / ROWB;             // rows per 64-lane 16-byte load
   static constexpr int LOADS = TILEB / 1024 / NW;     // loads per wave per tile, each tensor
   static_assert(LOADS >= 1 && TILEB % (1024 * NW) == 0, "tile must split evenly over waves");
@@ -131,8 +139,6 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
   // compiler cannot tell which stage an LDS-direct load fills, and would make
   // compiler-visible reads wait for all loads in flight.)
   __shared__ __attribute__((aligned(1024))) char smem[2 * NS * C::TILEB];
-  // Per query tile of the workgroup: 1 = recompute it by the exact path.
-  __shared__ int redo_flag[2];
   auto k_tile = [&](auto S) -> lds_char* { return (lds_char*)smem + decltype(S)::value * C::TILEB; };
   auto v_tile = [&](auto S) -> lds_char* {
     return (lds_char*)smem + (NS + decltype(S)::value) * C::TILEB;
@@ -143,10 +149,6 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
   const int lane = tid & 63;
   const int lc = lane & 31;  // query column inside a 32-block
   const int g = lane >> 5;   // half-wave
-  if (tid == 0) {
-    redo_flag[0] = 0;
-    redo_flag[1] = 0;
-  }
 
   // XCD-aware work decode: hardware deals workgroup ids round-robin over the
   // 8 XCDs, so id -> (id % 8) * (G / 8) + id / 8 keeps consecutive logical
@@ -350,7 +352,8 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
     // in issue order, and the wait before slice s allows the reads issued
     // after it).  Used where no other LDS read is in flight.
     auto qk = [&](f32x16 (&sacc)[NB], auto S) {
-      constexpr int OFF = decltype(S)::value * C::TILEB;
+      constexpr int OFF = C::template stage_lo<decltype(S)::value>;
+      constexpr uint32_t HI = C::template stage_hi<decltype(S)::value>;
       constexpr int NR = D / 16, PF = NR < 6 ? NR : 6;
       bf16x8 a[NR];
 #pragma unroll
@@ -358,12 +361,12 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
       // (Explicit captures: clang does not capture variables that a generic
       // lambda uses only as inline-assembly operands.)
       static_for<0, PF>([&a, &kaddr](auto I) {
-        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(a[I]) : "v"(kaddr[I]), "n"(OFF));
+        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(a[I]) : "v"(kaddr[I] + HI), "n"(OFF));
       });
       static_for<0, NR>([&a, &kaddr, &sacc, &qreg](auto I) {
         constexpr int sl = decltype(I)::value;
         if constexpr (sl + PF < NR)
-          asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(a[sl + PF]) : "v"(kaddr[sl + PF]), "n"(OFF));
+          asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(a[sl + PF]) : "v"(kaddr[sl + PF] + HI), "n"(OFF));
         constexpr int issued = sl + PF < NR ? sl + PF + 1 : NR;
         asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a[sl]) : "n"(issued - sl - 1));
 #pragma unroll
@@ -460,14 +463,15 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
     // The transposing reads of the V tile in stage S (for each 32-wide slice
     // of d, two 16-key halves of 8 rows each).
     auto v_reads = [&vaddr](auto S, bf16x8 (&va)[D / 32][2]) {
-      constexpr int OFF = decltype(S)::value * C::TILEB;
+      constexpr int OFF = C::template stage_lo<decltype(S)::value>;
+      constexpr uint32_t HI = C::template stage_hi<decltype(S)::value>;
       static_for<0, D / 32>([&vaddr, &va](auto DB) {
         static_for<0, 2>([&vaddr, &va](auto K16) {
           constexpr int db = decltype(DB)::value, k16 = decltype(K16)::value;
           constexpr int o = OFF + k16 * 16 * C::ROWB;
           bf16x4 lo, hi;
-          asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(vaddr[db]), "n"(o));
-          asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(vaddr[db]), "n"(o + 8 * C::ROWB));
+          asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(vaddr[db] + HI), "n"(o));
+          asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(vaddr[db] + HI), "n"(o + 8 * C::ROWB));
           va[db][k16] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         });
       });
@@ -495,9 +499,10 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
     // step's LDS reads split between its halves -- V beside the score
     // products, K beside the value product.
     auto k_reads = [&kaddr](auto S, bf16x8 (&kf)[D / 16]) {
-      constexpr int OFF = decltype(S)::value * C::TILEB;
+      constexpr int OFF = C::template stage_lo<decltype(S)::value>;
+      constexpr uint32_t HI = C::template stage_hi<decltype(S)::value>;
       static_for<0, D / 16>([&kaddr, &kf](auto I) {
-        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(kf[I]) : "v"(kaddr[I]), "n"(OFF));
+        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(kf[I]) : "v"(kaddr[I] + HI), "n"(OFF));
       });
     };
     // S^T = K Q^T from fragments read by k_reads a step earlier (the last LDS
@@ -731,9 +736,24 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
           for (int e2 = 0; e2 < 16; ++e2) z = __builtin_fmaf(oacc[db][nb][e2], 0.f, z);
       }
       bad |= !(z == 0.f);  // inf * 0 and NaN * 0 are NaN
-      if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) redo_flag[qi] = 1;
+      // Each wave's vote in a slot of the last K stage: its loads have all
+      // landed (the barrier above), and the next query tile's first loads
+      // fill the first AHEAD stages only, so every wave has read the votes
+      // before anything is written there again.  (Inline assembly like every
+      // other access to the ring, each access awaited in its own block.)
+      const uint32_t votes = lds0 + (NS - 1) * C::TILEB;
+      const uint32_t my_vote = __builtin_amdgcn_ballot_w64(bad) != 0 ? 1u : 0u;
+      if (lane == 0)
+        asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(votes + 4 * wave), "v"(my_vote) : "memory");
       __syncthreads();
-      if (redo_flag[qi]) exact_pass();
+      uint32_t redo = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        uint32_t vw;
+        asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(vw) : "v"(votes + 4 * w) : "memory");
+        redo |= vw;
+      }
+      if (redo) exact_pass();
     } else if (n_tiles > 0) {
       exact_pass();
     }
