@@ -317,8 +317,8 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
       x.vb = (const __bf16*)block_v(x.t) + kv_off;
     };
     auto advance = [&](Tile x, auto WithAddrs) {
-      if (x.t >= t1) return x;
-      if (++x.kt < x.vis) return x;
+      if (__builtin_expect(x.t >= t1, 0)) return x;
+      if (__builtin_expect(++x.kt < x.vis, 1)) return x;
       x.kt = 0;
       while (++x.t < t1) {
         block_counts(x);
@@ -656,7 +656,7 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
           // i-1, released by the barrier that closed step i-1.
           static_for<0, G>([&](auto J) {
             constexpr int jx = decltype(J)::value;
-            if (i + C::AHEAD + jx < n_tiles) issue_loads(Ic<(k + C::AHEAD + jx) % NS>{}, ld);
+            if (__builtin_expect(i + C::AHEAD + jx < n_tiles, 1)) issue_loads(Ic<(k + C::AHEAD + jx) % NS>{}, ld);
             ld = advance(ld, Ic<1>{});
           });
           // Measurement mode: no overlap of the tile transfers with compute.
@@ -704,10 +704,10 @@ __global__ __launch_bounds__(NW * 64, RA_FWD_WPE) void fwd_bf16_kernel(FwdParams
           bool high = false;
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) high |= l_part[nb] > kRaiseAt;
-          if (__builtin_amdgcn_ballot_w64(high) != 0) raise_ref(bad, y);
+          if (__builtin_expect(__builtin_amdgcn_ballot_w64(high) != 0, 0)) raise_ref(bad, y);
         }
-        if (++i >= n_tiles) return false;
-        if (nx.kt >= nx.full) mask(y, nx);  // tile i (the next step's x)
+        if (__builtin_expect(++i >= n_tiles, 0)) return false;
+        if (__builtin_expect(nx.kt >= nx.full, 0)) mask(y, nx);  // tile i (the next step's x)
         nx = advance(nx, Ic<0>{});
         return true;
       };
