@@ -17,12 +17,14 @@ pytestmark = pytest.mark.gpu
 LOG2E = 1.4426950408889634
 
 
-def rising_problem(S, c, split, Hq, Hkv, d, rank, step_log2, last_extra_log2=0.0, seed=7):
+def rising_problem(S, c, split, Hq, Hkv, d, rank, step_log2, last_extra_log2=0.0, seed=7,
+                   boosted_queries=None):
     """Q, K, V ~ N(0, 1) plus a shared direction: q[., 0] += a for every
-    query and k[., 0] += b_t for the keys of the block the ring delivers at
-    step t to `rank`, with a * b_t * scale * log2(e) = t * step_log2 (+ an
-    extra jump on the last block).  So the score of a key visited at step t
-    exceeds those of step 0 by about t * step_log2 log2 units."""
+    query (or for the natural positions in `boosted_queries`) and
+    k[., 0] += b_t for the keys of the block the ring delivers at step t to
+    `rank`, with a * b_t * scale * log2(e) = t * step_log2 (+ an extra jump on
+    the last block).  So the score of a key visited at step t exceeds those of
+    step 0 by about t * step_log2 log2 units for a boosted query."""
     g = np.random.default_rng(seed)
     q = g.standard_normal((1, Hq, S, d), dtype=np.float32)
     k = g.standard_normal((1, Hkv, S, d), dtype=np.float32)
@@ -36,7 +38,10 @@ def rising_problem(S, c, split, Hq, Hkv, d, rank, step_log2, last_extra_log2=0.0
     t = (rank - owner) % c
     b = t * step_log2 / (a * scale * LOG2E)
     b = b + (t == c - 1) * last_extra_log2 / (a * scale * LOG2E)
-    q[..., 0] += a
+    if boosted_queries is None:
+        q[..., 0] += a
+    else:
+        q[..., boosted_queries, 0] += a
     k[..., 0] += b[None, None, :].astype(np.float32)
     return Problem(S, c, split, 1, Hq, Hkv, d, "bf16", arrays=(q, k, v))
 
@@ -81,6 +86,38 @@ def test_jump_beyond_fp32_range_takes_exact_path(causal):
         compare(out, lse, ref_o, ref_l, tol=TOL["bf16"])
         exact += st.cpu().tolist()[5]
     assert exact > 0, "the exact per-tile path never ran"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("order", ["fast_then_exact", "exact_then_fast"])
+def test_exact_path_beside_a_fast_tile_in_one_workgroup(d, order):
+    """4 096 tokens over 4 shards: four 256-row query tiles per (head, shard),
+    two per workgroup (tiles p and 3 - p, the first from the first half of the
+    sequence).  Only the query tiles that meet the 200-log2-unit jump of the
+    last block overflow, so a workgroup recomputes one of its tiles by the
+    exact path and runs the other on the fast path.  Causal with every query
+    boosted: the second tile (later positions) is the one that sees the jump.
+    Bidirectional with only first-half queries boosted: the first tile is
+    recomputed and the next tile's first loads follow its exact pass.  Every
+    row must match the oracle, and the exact path must run for exactly the
+    tiles that overflow."""
+    S, c, split, Hq, Hkv = 4096, 4, ra.SPLIT_ZIGZAG, 2, 1
+    causal = order == "fast_then_exact"
+    boosted = None if causal else np.arange(S // 2)
+    exact, tiles = 0, 0
+    for r in range(c):
+        p = rising_problem(S, c, split, Hq, Hkv, d, r, step_log2=5.0, last_extra_log2=200.0, seed=13,
+                           boosted_queries=boosted)
+        say(f"exact beside fast d={d} {order} rank {r}")
+        out, lse, st = p.run(r, causal=causal, flags=ra.FLAG_EVENT_COUNTS)
+        ref_o, ref_l = p.reference(r, causal=causal)
+        compare(out, lse, ref_o, ref_l, tol=TOL["bf16"])
+        exact += st.cpu().tolist()[5]
+        tiles += Hq * (p.n_loc // ra.ring_attn_tile_shape(p.desc())[0])
+    assert 0 < exact < tiles, f"{exact} of {tiles} query tiles took the exact path"
+    if not causal:
+        # Every first-half tile (boosted) overflows; no second-half tile does.
+        assert exact == tiles // 2, f"{exact} of {tiles} query tiles took the exact path"
 
 
 def test_event_counts_are_zero_on_the_benchmark_distribution():
