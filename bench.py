@@ -134,8 +134,8 @@ def host_info():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="s128k_c16_zigzag_16x1", choices=sorted(workloads.WORKLOAD_BY_NAME))
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle CPU-baseline budget (0: skip)")
     ap.add_argument("--suite", action="store_true",
