@@ -310,12 +310,13 @@ def test_merge_in_place_and_identity():
 @pytest.mark.parametrize("c", [1, 2])
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
 def test_pipeline_ends_at_every_step(d, c, causal):
-    """Shard lengths 32 .. 480 (1 .. 15 visible 32-key tiles per block and one
-    or two query tiles per workgroup): the tile pipeline, unrolled over six
-    steps with K fragments read a step ahead, ends at every position of its
-    unrolled loop.  Every row of every rank against the oracle, and the work
+    """Shard lengths 32 .. 672 (1 .. 21 visible 32-key tiles per block and one
+    or two query tiles per workgroup): the tile pipeline, unrolled over twenty
+    steps (ten LDS stages, two score buffers, a barrier every four steps) with
+    K fragments read a step ahead, ends at every position of its unrolled
+    loop.  Every row of every rank against the oracle, and the work
     counters."""
-    for n_loc in range(32, 481, 32):
+    for n_loc in range(32, 673, 32):
         S = n_loc * c
         p = Problem(S, c, ra.SPLIT_CONTIGUOUS, 1, 2, 1, d, "bf16", seed=S + c + d)
         tq, tk = ra.ring_attn_tile_shape(p.desc(causal=causal))
