@@ -71,14 +71,17 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(DecodeParams p) 
 
   // LDS-direct load roles: lane -> (row in its 1 KiB group, 16-byte slot).
   const int ld_row = lane / Z::CHUNKS, ld_slot = lane % Z::CHUNKS;
+  // The tile offset is part of each lane's offset (not the scalar offset,
+  // which the buffer range check does not cover), so rows past the block end
+  // read as zeros: the last tile of a range may run past it.
   auto issue = [&](int j, int st) {
-    const uint32_t soff = (uint32_t)(k0 + 32 * j) * ROWB;
+    const uint32_t toff = (uint32_t)(k0 + 32 * j) * ROWB;
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int row = u * RPI + ld_row;
-      lds_load16_nt(rk, base + st * 2 * TILEB + u * 1024, row * ROWB + Z::k_slot(row, ld_slot) * 16, soff);
-      lds_load16_nt(rv, base + st * 2 * TILEB + TILEB + u * 1024, row * ROWB + Z::v_slot(row, ld_slot) * 16,
-                    soff);
+      lds_load16_nt(rk, base + st * 2 * TILEB + u * 1024, toff + row * ROWB + Z::k_slot(row, ld_slot) * 16, 0);
+      lds_load16_nt(rv, base + st * 2 * TILEB + TILEB + u * 1024,
+                    toff + row * ROWB + Z::v_slot(row, ld_slot) * 16, 0);
     }
   };
 

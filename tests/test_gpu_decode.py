@@ -82,6 +82,39 @@ def test_decode_parts_and_merge(S, c, split, B, Hq, Hkv, d, n_splits):
     compare(out[:, :, None], lse[:, :, None], ref_o, ref_l, tol=TOL["bf16"])
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n_splits", [1, 3])
+def test_decode_ragged_block_end_before_nan_guard(d, n_splits):
+    """Blocks of 250 keys (the last 32-key tile of a block is 26 rows long),
+    each the start of a buffer whose following rows are NaN: the last tile of
+    every range that ends at the block end reads past it, and those rows must
+    read as zeros (the buffer range check), so every partial and the merge
+    stay finite and match the oracle."""
+    S, c, split, B, Hq, Hkv = 1000, 4, ra.SPLIT_CONTIGUOUS, 1, 4, 1
+    p = Decode(S, c, split, B, Hq, Hkv, d, seed=41)
+    guarded = {}
+    for name, src in (("k", p.ks), ("v", p.vs)):
+        guarded[name] = []
+        for t in range(c):
+            buf = torch.full((B, Hkv, p.n + 64, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+            buf[:, :, :p.n] = src[t]
+            blk = buf.reshape(-1)[: B * Hkv * p.n * d].view(B, Hkv, p.n, d)  # B = Hkv = 1: block, then NaN rows
+            guarded[name].append((blk, buf))
+    torch.cuda.synchronize()
+    say(f"decode NaN guard d={d} splits={n_splits}")
+    n_parts = c * n_splits
+    outs = torch.full((n_parts, B, Hq, d), float("nan"), dtype=torch.float32, device=DEV)
+    lses = torch.full((n_parts, B, Hq), float("nan"), dtype=torch.float32, device=DEV)
+    ra.ring_attn_decode(p.desc(), p.qd, [kb for kb, _ in guarded["k"]], [vb for vb, _ in guarded["v"]],
+                        n_splits, outs, lses)
+    torch.cuda.synchronize()
+    assert torch.isfinite(outs).all() and torch.isfinite(lses).all()
+    check_parts(p, list(range(c)), n_splits, outs, lses)
+    out, lse = p.merged(outs, lses)
+    ref_o, ref_l = p.ref()
+    compare(out[:, :, None], lse[:, :, None], ref_o, ref_l, tol=TOL["bf16"])
+
+
 def test_decode_maximum_block_count():
     p = Decode(8192, 128, ra.SPLIT_ZIGZAG, 1, 8, 1, 128, seed=9)
     outs, lses = p.run(list(range(128)), 2)
