@@ -208,19 +208,25 @@ def main():
     vb = [[vs[j] for j in owners[r]] for r in range(c)]
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(c)]
 
-    def step(timed_kernels):
+    batch_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+
+    def step(timed_kernels=False, timed_batch=False):
         ra.zigzag_partition(w.seq_len, c, w.split, None, qn, qs, w.batch * w.h_q, w.head_dim * esz)
         ra.zigzag_partition(w.seq_len, c, w.split, None, kn, ks, w.batch * w.h_kv, w.head_dim * esz)
         ra.zigzag_partition(w.seq_len, c, w.split, None, vn, vs, w.batch * w.h_kv, w.head_dim * esz)
+        if timed_batch:
+            batch_ev[0].record()
         for r in range(c):
             if timed_kernels:
                 ev[r][0].record()
             ra.ring_attn_shard_fwd(desc, r, qs[r], kb[r], vb[r], out, lse, stats=stats)
             if timed_kernels:
                 ev[r][1].record()
+        if timed_batch:
+            batch_ev[1].record()
 
     for _ in range(args.warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
     stats.zero_()
 
@@ -228,15 +234,22 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(False)
+        step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     st = stats.cpu().tolist()
 
-    # Kernel durations with HIP events on the launch stream (a separate pass).
-    kernel_ms = []
+    # Kernel durations with HIP events on the launch stream (separate passes):
+    # one event pair around each step's c back-to-back launches gives the
+    # average (no event between launches), one pair around each launch the
+    # median and minimum.
+    kernel_ms, batch_ms = [], []
     for _ in range(max(1, min(args.steps, 3))):
-        step(True)
+        step(timed_batch=True)
+        torch.cuda.synchronize()
+        batch_ms.append(batch_ev[0].elapsed_time(batch_ev[1]) / c)
+    for _ in range(max(1, min(args.steps, 3))):
+        step(timed_kernels=True)
         torch.cuda.synchronize()
         kernel_ms.extend(ev[r][0].elapsed_time(ev[r][1]) for r in range(c))
 
@@ -247,7 +260,7 @@ def main():
         raise SystemExit(f"kernel pair count {pairs_counted} != {sum(pairs) * w.h_q * w.batch}")
     ms_step = elapsed * 1e3 / args.steps
     value = flop_step / (elapsed / args.steps) / 1e12
-    avg_kernel_s = float(np.mean(kernel_ms)) / 1e3
+    avg_kernel_s = float(np.mean(batch_ms)) / 1e3
     flop_launch = flop_step / c
     achieved = flop_launch / avg_kernel_s / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -268,7 +281,8 @@ def main():
                      "flop_per_launch": flop_launch, "avg_launch_ms": round(avg_kernel_s * 1e3, 4),
                      "median_launch_ms": round(float(np.median(kernel_ms)), 4),
                      "min_launch_ms": round(float(np.min(kernel_ms)), 4),
-                     "launches_timed": len(kernel_ms),
+                     "launches_timed": len(batch_ms) * c,
+                     "per_launch_event_avg_ms": round(float(np.mean(kernel_ms)), 4),
                      "held_shader_clock_ghz": measured_clock() if w.name == "s128k_c16_zigzag_16x1" else None},
         "stats_per_step": {"pairs": int(pairs_counted), "tiles_full": st[1] // args.steps,
                            "tiles_partial": st[2] // args.steps, "tiles_skipped": st[3] // args.steps},
